@@ -1,0 +1,29 @@
+"""CPU float64 oracle for exact scaled dot-product attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path imports, calls or links this
+package: only the tests, the smoke entry point and the bench's CPU baseline leg may.
+It shares no code, constant or helper with the HIP path.
+
+Contents
+--------
+attention         The plain definition: S = scale*Q K^T with the causal and key-padding
+                  masks, safe softmax, O = P V, LSE = m + ln(l), and the chain-rule
+                  backward. Materialises S and P (per head, in row blocks).
+page_algorithms   The softmax / attention recurrences the pages derive (3-pass safe
+                  softmax, 2-pass online softmax, 2-pass and 1-pass FlashAttention rows,
+                  the tiled recurrence, the Br x Bc block update, the statistics merge),
+                  written as scalar float64 loops. They cross-check the definition.
+
+Every function is pinned by tests in tests/test_oracle_*.py against closed forms,
+invariants, brute force, finite differences, independent library routines and
+hand-derived fixtures in tests/golden/. No function here is "parity unpinned".
+"""
+from .attention import (  # noqa: F401
+    allowed_mask,
+    head_forward,
+    head_backward,
+    attention_forward,
+    attention_backward,
+    attention_forward_heads,
+    attention_backward_heads,
+)
