@@ -1,0 +1,216 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+A step is one pass of the whole path on one batch: fa_fwd (forward, O and LSE) then
+fa_bwd (D = rowsum(dO*O), recompute, dQ/dK/dV) on the workload B=2, H=16, N=4096,
+d=128, causal, bf16 inputs with Q scaled x4 (inputs drawn once with the seeded
+generator and resident in HBM before timing). The metric is attention TFLOP/s under
+the nominal count 4*B*H*N^2*d (halved when causal) for the forward pass plus 2.5x
+that for the backward pass, against the dense bf16 matrix-core peak.
+
+Prints ONE JSON line with the throughput, the roofline of the dominant call
+(measured with HIP events on the stream the kernels run on) and the CPU oracle's
+throughput on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--sweep] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0
+WORKLOAD_ID = 4
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "counters_b2h16_n4096_d128_causal.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "io_aware_softmax_tiled_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, launches_per_step: int = 1):
+    """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs, scaled by
+    the copy-kernel calibration, or None when absent or taken on other kernel sources."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, w, budget_heads=None):
+    """Time the CPU oracle (as it stands) on a bounded sample of heads of the workload."""
+    import oracle
+    import workloads
+
+    workers = oracle.attention.default_workers()
+    nheads = budget_heads or min(w.B * w.H, max(2, workers))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:nheads]
+    q, k, v, do = (workloads.as_f64(inp[n]) for n in ("q", "k", "v", "dout"))
+    t0 = time.perf_counter()
+    oracle.attention_forward_heads(q, k, v, w.scale, w.causal, None, heads=heads,
+                                   workers=workers)
+    oracle.attention_backward_heads(q, k, v, do, w.scale, w.causal, None, heads=heads,
+                                    workers=workers)
+    dt = time.perf_counter() - t0
+    per_head = (w.fwd_flops() + w.bwd_flops()) / (w.B * w.H)
+    return {
+        "value": round(per_head * nheads / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": min(workers, nheads),
+        "kind": "oracle",
+        "sample": f"{nheads} of {w.B * w.H} heads of the same workload, forward + backward, "
+                  f"float64 numpy, {dt:.1f} s wall",
+    }
+
+
+def run_step(fa, dev, w, ws, events=None):
+    o, lse = fa.fa_fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale,
+                       out=dev["o"], lse=dev["lse"])
+    if events is not None:
+        events[1].record()
+    dq, dk, dv = fa.fa_bwd(dev["q"], dev["k"], dev["v"], o, dev["dout"], lse,
+                           causal=w.causal, scale=w.scale, workspace=ws)
+    if events is not None:
+        events[2].record()
+    return dq
+
+
+def bench_workload(fa, torch, w, inp, steps, warmup):
+    dev = {n: inp[n].cuda() for n in ("q", "k", "v", "dout")}
+    dev["o"] = torch.empty(dev["q"].shape, dtype=torch.float32, device="cuda")
+    dev["lse"] = torch.empty(dev["q"].shape[:3], dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(warmup):
+        run_step(fa, dev, w, ws)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        run_step(fa, dev, w, ws, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [a.elapsed_time(b) for a, b, _ in evs]
+    bwd_ms = [b.elapsed_time(c) for _, b, c in evs]
+    return wall * 1e3 / steps, sum(fwd_ms) / steps, sum(bwd_ms) / steps
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sweep", action="store_true",
+                    help="also print one line per sequence length (supplementary)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(heads shard across GPUs with no exchange; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import io_aware_softmax_tiled_amd as fa
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.load_library()
+    w = workloads.WORKLOADS[WORKLOAD_ID]
+    inp = workloads.draw(w)
+    ms_step, fwd_ms, bwd_ms = bench_workload(fa, torch, w, inp, args.steps, args.warmup)
+
+    fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
+    value = (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
+    fwd_tf = fwd_f / (fwd_ms * 1e-3) / 1e12
+    bwd_tf = bwd_f / (bwd_ms * 1e-3) / 1e12
+    # the dominant call of the step; its kernels: fwd = one kernel, bwd = pre + main
+    if bwd_ms >= fwd_ms:
+        dom = {"kernel": "fa_bwd (bwd_pre_kernel + bwd_main_kernel)", "ms": bwd_ms,
+               "flops": bwd_f, "traffic_key": "fa_bwd"}
+    else:
+        dom = {"kernel": "fwd_kernel_16", "ms": fwd_ms, "flops": fwd_f,
+               "traffic_key": "fa_fwd"}
+    achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": measured_traffic(dom["traffic_key"]),
+        "kernel": dom["kernel"],
+        "avg_launch_ms": round(dom["ms"], 4),
+    }
+    line = {
+        "metric": "attention fwd+bwd TFLOP/s (nominal 4BHN^2d/2 causal fwd + 2.5x bwd) and "
+                  "% of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded i.i.d. N(0,1), Q x4)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "passes": "fwd+bwd"},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "passes": {"fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tf, 2),
+                           "pct_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2)},
+                   "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 2),
+                           "pct_peak": round(100 * bwd_tf / PEAK_BF16_TFLOPS, 2)}},
+        "roofline": roofline,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(inp, w),
+    }
+    print(json.dumps(line), flush=True)
+
+    if args.sweep:
+        sweep(fa, torch, workloads)
+
+
+def sweep(fa, torch, workloads):
+    """Supplementary lines: TFLOP/s vs sequence length at 16K tokens x 2048 hidden."""
+    for d in (64, 128):
+        for causal in (False, True):
+            for N in (512, 1024, 2048, 4096, 8192, 16384):
+                B, H = max(1, 16384 // N), 2048 // d
+                w, inp = workloads.custom(B, H, N, d, "bf16", causal, seed=0)
+                ms_step, fwd_ms, bwd_ms = bench_workload(fa, torch, w, inp, 10, 3)
+                print(json.dumps({
+                    "sweep": True, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                    "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+                    "fwd_tflops": round(w.fwd_flops() / fwd_ms / 1e9, 2),
+                    "bwd_tflops": round(w.bwd_flops() / bwd_ms / 1e9, 2)}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,120 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library libfa_mi355x.so.
+ *
+ * What it computes. For every batch b and head h, with Q, K, V of shape [N, d]:
+ *   S = scale * Q K^T, with S_ij = -inf where key j is not visible to query i,
+ *   P = softmax(S) row by row, O = P V, LSE_i = ln sum_j exp(S_ij),
+ * and the gradient of L = sum(dO * O) with respect to Q, K and V.
+ * "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness"
+ * (summary of arXiv 2205.14135), Problem and motivation, defines S, P and O; its FAQ
+ * states that the tiled method returns this same exact result; its Key ideas section
+ * fixes what the backward pass gets from the forward pass (O and the softmax
+ * statistics, here folded into LSE). "[Review] From Online Softmax to Flash
+ * Attention", sections FlashAttention and Algorithm FlashAttention (Tiling), gives
+ * the online-softmax recurrence the forward kernel runs.
+ *
+ * Visibility. Key j is visible to query i iff (causal == 0 || j <= i) and
+ * (kv_len == NULL || j < kv_len[b]). The causal rule is the lower-triangular mask
+ * tril(ones, 0) of "Fewer matrix multiplications, same results" (flash-attention
+ * issue #941), diagonal included, top-left aligned; keys at or past kv_len[b] are
+ * scored -inf like the out-of-range keys of the review's Triton listings.
+ *
+ * Layout. q, k, v, dout, o, dq, dk, dv are dense row-major [B, H, N, d] (the
+ * [batch, heads, seq, head_dim] order of the issue's listing); lse is [B, H, N].
+ * q, k, v and dout share one element type (dtype); o, lse, dq, dk, dv are float32.
+ *
+ * Pointers. Every tensor pointer is device memory owned by the caller; the library
+ * keeps no pointer after a call returns. kv_len, when not NULL, is a device array
+ * of B int32 values, each in [1, N] (not checked on the host: reading it would need
+ * a copy). Tensor pointers must be 16-byte aligned, lse and kv_len 4-byte aligned.
+ * Outputs must not overlap inputs or each other (checked). The library allocates
+ * nothing and keeps no state between calls; calls are thread-safe.
+ *
+ * Streams. `stream` is a hipStream_t (NULL: the null stream). Every entry point
+ * only validates on the host and enqueues; it returns before the GPU work ends, and
+ * a device fault shows up at the caller's next synchronisation.
+ *
+ * Errors. Entry points return FA_OK or an error code; on error nothing has been
+ * enqueued and fa_last_error() (thread-local) says why.
+ *
+ * Limits. d in {64, 128}; scale finite and > 0; B, H, N >= 0 (a zero size makes
+ * the call a no-op); B*H*N*d < 2^40; N <= 2^22. bf16/f16 inputs are read exactly;
+ * internally P and dS are rounded to fp16 for the matrix cores, and bf16 operands
+ * they multiply are converted to fp16, which is exact when every |x| of V, dO, Q and
+ * K lies in [2^-14, 65504] or is 0 (smaller magnitudes lose low bits).
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define FA_API __attribute__((visibility("default")))
+#else
+#define FA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and dout. */
+enum fa_dtype { FA_F32 = 0, FA_BF16 = 1, FA_F16 = 2 };
+
+/* Status codes. */
+enum fa_status {
+  FA_OK = 0,
+  FA_EINVAL = 1,        /* null pointer, bad size, misalignment, overlap, bad scale */
+  FA_EUNSUPPORTED = 2,  /* head_dim or dtype the library has no kernel for */
+  FA_EWORKSPACE = 3,    /* backward workspace missing or too small */
+  FA_EHIP = 4           /* the HIP runtime reported an error at launch */
+};
+
+/*
+ * Forward pass. Writes o [B,H,N,d] float32 (O = P V) and lse [B,H,N] float32
+ * (natural-log log-sum-exp of the scaled, masked scores of each query row).
+ * The N x N score matrix never leaves the chip: each workgroup keeps a block of
+ * query rows and streams key/value tiles through the online-softmax recurrence
+ * (running row maximum, running denominator, rescaled output accumulator).
+ */
+FA_API int fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           const int32_t* kv_len, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes (the per-row
+ * D_i = sum_k dO_ik O_ik, float32 [B,H,N], rounded up to 256 bytes).
+ */
+FA_API size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Backward pass of L = sum(dout * O). Inputs: q, k, v, dout (dtype), o and lse
+ * exactly as fa_fwd wrote them for the same q, k, v, scale, causal and kv_len.
+ * Outputs (float32, overwritten): dq, dk, dv [B,H,N,d]. The scores and
+ * probabilities are recomputed on chip from q, k and lse, tile by tile.
+ * workspace: device memory of at least fa_bwd_workspace_size(B,H,N,d) bytes,
+ * 256-byte aligned, owned by the caller, contents on entry irrelevant.
+ * dq is accumulated with float32 atomics, so its last bits may differ from run
+ * to run; dk and dv are deterministic.
+ */
+FA_API int fa_bwd(const void* q, const void* k, const void* v, const float* o,
+           const void* dout, const float* lse, float* dq, float* dk, float* dv,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           const int32_t* kv_len, void* workspace, size_t workspace_bytes,
+           void* stream);
+
+/* Static description of a status code. */
+FA_API const char* fa_status_str(int status);
+
+/* Detail of the last error returned on this thread ("" when none). */
+FA_API const char* fa_last_error(void);
+
+/* Library version: major*10000 + minor*100 + patch. */
+FA_API int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

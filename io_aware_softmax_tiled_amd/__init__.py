@@ -1,0 +1,170 @@
+"""Exact attention (forward and backward) on MI355X: Python binding of libfa_mi355x.so.
+
+This module only marshals arguments: it allocates outputs with torch on the inputs'
+device, passes raw device pointers and the current HIP stream to the C ABI declared in
+include/fa.h, and raises on a nonzero status. Every step of the computation runs in
+the library's HIP kernels; there is no CPU or PyTorch fallback, and importing a
+function here fails loudly when the library has not been built
+(python -m io_aware_softmax_tiled_amd.build).
+
+Functions have the C entry points' names:
+    fa_fwd(q, k, v, *, causal=False, scale=None, kv_len=None) -> (o, lse)
+    fa_bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, kv_len=None) -> (dq, dk, dv)
+    fa_bwd_workspace_size(B, H, N, d) -> int
+    fa_status_str(code) -> str, fa_last_error() -> str, fa_version() -> int
+Tensors are [B, H, N, d] contiguous (q, k, v, dout: float32, bfloat16 or float16;
+o, dq, dk, dv: float32), lse is [B, H, N] float32, kv_len an int32 [B] device tensor
+or None. The default scale is 1/sqrt(d).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_str", "fa_last_error",
+           "fa_version", "FaError", "lib_path", "load_library",
+           "FA_F32", "FA_BF16", "FA_F16"]
+
+FA_F32, FA_BF16, FA_F16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.float16: FA_F16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libfa_mi355x.so")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{fa_status_str(status)}: {detail}")
+        self.status = status
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libfa_mi355x.so once and declare the C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m io_aware_softmax_tiled_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, i32, vp, vp]
+    lib.fa_fwd.restype = i32
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32,
+                           i32, vp, vp, sz, vp]
+    lib.fa_bwd.restype = i32
+    lib.fa_bwd_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_status_str.argtypes = [i32]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i32
+    _LIB = lib
+    return lib
+
+
+def fa_status_str(code: int) -> str:
+    return load_library().fa_status_str(int(code)).decode()
+
+
+def fa_last_error() -> str:
+    return load_library().fa_last_error().decode()
+
+
+def fa_version() -> int:
+    return int(load_library().fa_version())
+
+
+def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().fa_bwd_workspace_size(B, H, N, d))
+
+
+def _check(status: int):
+    if status != 0:
+        raise FaError(status, fa_last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _shape(q, k, v):
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"shape mismatch: q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE_CODE:
+        raise ValueError("q, k, v must share one dtype among float32, bfloat16, float16")
+    for t in (q, k, v):
+        if not t.is_cuda:
+            raise ValueError("inputs must be GPU tensors")
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    return tuple(int(x) for x in q.shape)
+
+
+def _kv(kv_len, B, device):
+    if kv_len is None:
+        return None
+    if kv_len.dtype != torch.int32 or kv_len.device != device or kv_len.numel() != B:
+        raise ValueError("kv_len must be an int32 tensor of B elements on the inputs' device")
+    return kv_len.contiguous()
+
+
+def _stream(device, stream):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def fa_fwd(q, k, v, *, causal=False, scale=None, kv_len=None, out=None, lse=None,
+           stream=None):
+    """Forward pass: returns (o float32 [B,H,N,d], lse float32 [B,H,N])."""
+    B, H, N, d = _shape(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    kv = _kv(kv_len, B, q.device)
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d, scale,
+                        int(bool(causal)), _DTYPE_CODE[q.dtype], _ptr(kv),
+                        _stream(q.device, stream))
+    _check(st)
+    return o, lse_t
+
+
+def fa_bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, kv_len=None, workspace=None,
+           stream=None):
+    """Backward pass of sum(dout * O): returns (dq, dk, dv), float32 [B,H,N,d]."""
+    B, H, N, d = _shape(q, k, v)
+    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
+        raise ValueError("dout must match q in shape and dtype and be contiguous")
+    if o.dtype != torch.float32 or lse.dtype != torch.float32:
+        raise ValueError("o and lse must be the float32 outputs of fa_fwd")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    kv = _kv(kv_len, B, q.device)
+    ws_bytes = fa_bwd_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                        _ptr(dk), _ptr(dv), B, H, N, d, scale, int(bool(causal)),
+                        _DTYPE_CODE[q.dtype], _ptr(kv), _ptr(workspace),
+                        workspace.numel() * workspace.element_size(),
+                        _stream(q.device, stream))
+    _check(st)
+    return dq, dk, dv

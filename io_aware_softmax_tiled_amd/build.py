@@ -1,0 +1,70 @@
+"""Build libfa_mi355x.so (HIP kernels for gfx950 + the C ABI) in this directory.
+
+Usage: python -m io_aware_softmax_tiled_amd.build   (or python io_aware_softmax_tiled_amd/build.py)
+Needs hipcc from ROCm; cross-compiles for gfx950 without a GPU present.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB_NAME = "libfa_mi355x.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
+ARCH = "gfx950"
+
+# -packed-fp32-ops: never emit packed fp32 VALU (v_pk_{add,mul,fma}_f32).
+# -munsafe-fp-atomics: fp32 atomic add lowers to the hardware atomic, not a CAS loop.
+HIPCC_FLAGS = [
+    "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-fvisibility=hidden",
+    "-munsafe-fp-atomics", "-Wall", "-Wno-unused-result",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the shared library; returns its path."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            cmd = [cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            if src.endswith(".cpp"):
+                cmd = [cc, "-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
+                       "-c", os.path.join(CSRC, src), "-o", obj]
+            _run(cmd, verbose)
+            objs.append(obj)
+        tmp_lib = os.path.join(tmp, LIB_NAME)
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib], verbose)
+        shutil.copyfile(tmp_lib, LIB_PATH + ".tmp")
+        os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature flag: drop that warning
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

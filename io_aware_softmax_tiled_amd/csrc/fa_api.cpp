@@ -1,0 +1,166 @@
+// C ABI of the exact-attention library: host-side validation, workspace sizing,
+// error strings, and dispatch to the kernel launchers. Nothing here allocates device
+// memory or keeps state between calls. The operations and the contract of every
+// entry point are documented in include/fa.h.
+#include "../../include/fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "fa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+size_t elem_size(int dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Span {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+bool overlap(const Span& a, const Span& b) {
+  if (a.bytes == 0 || b.bytes == 0) return false;
+  const auto a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Shared checks of sizes, dtype, head_dim and scale. Returns FA_OK or an error.
+int check_common(int B, int H, int N, int d, float scale, int dtype) {
+  if (B < 0 || H < 0 || N < 0)
+    return fail(FA_EINVAL, "sizes must be >= 0 (B=%d H=%d N=%d)", B, H, N);
+  if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16)
+    return fail(FA_EUNSUPPORTED, "unknown dtype code %d (0=f32, 1=bf16, 2=f16)", dtype);
+  if (d != 64 && d != 128) return fail(FA_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", d);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(FA_EINVAL, "scale must be finite and > 0 (got %g)", (double)scale);
+  if (N > (1 << 22)) return fail(FA_EINVAL, "N=%d exceeds the limit 2^22", N);
+  const double elems = (double)B * H * N * d;
+  if (elems >= 1099511627776.0) return fail(FA_EINVAL, "B*H*N*d too large");
+  // grid: 8 * ceil(B*H/8) * ceil(N/128) workgroups, and ceil(N/64) per head backward
+  const double blocks = 8.0 * std::ceil((double)B * H / 8.0) * std::ceil(N / 64.0);
+  if (blocks >= 2147483647.0) return fail(FA_EINVAL, "too many workgroups for one launch");
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_EINVAL: return "FA_EINVAL: invalid argument";
+    case FA_EUNSUPPORTED: return "FA_EUNSUPPORTED: unsupported head_dim or dtype";
+    case FA_EWORKSPACE: return "FA_EWORKSPACE: workspace missing or too small";
+    case FA_EHIP: return "FA_EHIP: HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+const char* fa_last_error(void) { return g_last_error; }
+
+int fa_version(void) { return 100; /* 0.1.0 */ }
+
+int fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
+           int N, int d, float scale, int causal, int dtype, const int32_t* kv_len,
+           void* stream) {
+  clear_error();
+  int st = check_common(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if ((size_t)B * H * N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return fail(FA_EINVAL, "null tensor pointer");
+  const size_t in_bytes = (size_t)B * H * N * d * elem_size(dtype);
+  const size_t o_bytes = (size_t)B * H * N * d * 4;
+  const size_t lse_bytes = (size_t)B * H * N * 4;
+  const Span ins[] = {{q, in_bytes, "q"}, {k, in_bytes, "k"}, {v, in_bytes, "v"},
+                      {kv_len, kv_len ? (size_t)B * 4 : 0, "kv_len"}};
+  const Span outs[] = {{o, o_bytes, "o"}, {lse, lse_bytes, "lse"}};
+  for (const Span& s : ins)
+    if (s.bytes && !aligned(s.p, s.p == kv_len ? 4 : 16))
+      return fail(FA_EINVAL, "%s is not %d-byte aligned", s.name, s.p == kv_len ? 4 : 16);
+  if (!aligned(o, 16)) return fail(FA_EINVAL, "o is not 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(FA_EINVAL, "lse is not 4-byte aligned");
+  for (const Span& a : outs) {
+    for (const Span& b : ins)
+      if (overlap(a, b)) return fail(FA_EINVAL, "output %s overlaps input %s", a.name, b.name);
+  }
+  if (overlap(outs[0], outs[1])) return fail(FA_EINVAL, "outputs o and lse overlap");
+
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal ? 1 : 0, dtype, kv_len};
+  hipError_t e = fa::launch_fwd(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_EHIP, "forward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
+  return fa::bwd_workspace_bytes(B, H, N, d);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const float* o, const void* dout,
+           const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+           float scale, int causal, int dtype, const int32_t* kv_len, void* workspace,
+           size_t workspace_bytes, void* stream) {
+  clear_error();
+  int st = check_common(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (dtype == FA_F32)
+    return fail(FA_EUNSUPPORTED, "the backward pass takes bf16 or f16 inputs, not f32");
+  if ((size_t)B * H * N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
+    return fail(FA_EINVAL, "null tensor pointer");
+  const size_t need = fa::bwd_workspace_bytes(B, H, N, d);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_EWORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(FA_EINVAL, "workspace is not 256-byte aligned");
+  const size_t in_bytes = (size_t)B * H * N * d * elem_size(dtype);
+  const size_t f_bytes = (size_t)B * H * N * d * 4;
+  const size_t lse_bytes = (size_t)B * H * N * 4;
+  const Span ins[] = {{q, in_bytes, "q"},       {k, in_bytes, "k"},         {v, in_bytes, "v"},
+                      {o, f_bytes, "o"},        {dout, in_bytes, "dout"},   {lse, lse_bytes, "lse"},
+                      {kv_len, kv_len ? (size_t)B * 4 : 0, "kv_len"}};
+  const Span outs[] = {{dq, f_bytes, "dq"}, {dk, f_bytes, "dk"}, {dv, f_bytes, "dv"},
+                       {workspace, need, "workspace"}};
+  for (const Span& s : ins) {
+    const size_t al = (s.p == kv_len || s.p == lse) ? 4 : 16;
+    if (s.bytes && !aligned(s.p, al)) return fail(FA_EINVAL, "%s is not %zu-byte aligned", s.name, al);
+  }
+  for (const Span& s : outs)
+    if (!aligned(s.p, 16)) return fail(FA_EINVAL, "%s is not 16-byte aligned", s.name);
+  for (int i = 0; i < 4; ++i) {
+    for (const Span& b : ins)
+      if (overlap(outs[i], b))
+        return fail(FA_EINVAL, "output %s overlaps input %s", outs[i].name, b.name);
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(FA_EINVAL, "outputs %s and %s overlap", outs[i].name, outs[j].name);
+  }
+
+  fa::BwdArgs a{q,  k,  v,  o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal ? 1 : 0,
+                dtype, kv_len, static_cast<float*>(workspace)};
+  hipError_t e = fa::launch_bwd(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_EHIP, "backward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+}  // extern "C"

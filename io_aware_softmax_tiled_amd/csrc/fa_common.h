@@ -1,0 +1,129 @@
+// Device-side helpers shared by the forward and backward kernels (gfx950 / CDNA4).
+//
+// Matrix-core conventions used throughout (checked on the device by a layout probe):
+//   v_mfma_f32_32x32x16_{bf16,f16}: C[32x32] += A[32x16] * B[16x32].
+//     lane l holds A[l%32][8*(l/32) + 0..7] and B[8*(l/32) + 0..7][l%32];
+//     accumulator register r of lane l is C[8*(r/4) + 4*(l/32) + r%4][l%32].
+//   v_mfma_f32_32x32x2f32: lane l holds A[l%32][l/32], B[l/32][l%32]; same C layout.
+//   ds_read_b64_tr_b16: inside each group of 16 lanes, lanes 4e..4e+3 point at four
+//     consecutive 4-element pieces of "row e"; lane i of the group receives element i
+//     of rows 0..3. This reads a row-major [key][d] tile as the [d][key] operand.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 16-bit element tag types: the storage is uint16_t; the tag selects the MFMA flavour.
+struct BF16 {};
+struct F16 {};
+
+template <typename T> struct Mfma;
+template <> struct Mfma<BF16> {
+  __device__ static inline f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // two fp32 -> packed pair, round to nearest even
+  __device__ static inline uint32_t pack(float lo, float hi) {
+    bf16x2 r = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, r);
+  }
+  // sum of a packed pair, accumulated in fp32
+  __device__ static inline float dot_ones(uint32_t p, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), one, acc, false);
+  }
+};
+template <> struct Mfma<F16> {
+  __device__ static inline f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack(float lo, float hi) {
+    f16x2 r = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, r);
+  }
+  __device__ static inline float dot_ones(uint32_t p, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), one, acc, false);
+  }
+};
+
+// bf16 pair -> f16 pair (exact for magnitudes in the fp16 normal range, and for 0)
+__device__ inline uint32_t bf16x2_to_f16x2(uint32_t x) {
+  const float lo = __uint_as_float(x << 16);
+  const float hi = __uint_as_float(x & 0xffff0000u);
+  f16x2 r = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Reductions across the two 32-lane halves of the wave. v_permlane32_swap with both
+// operands equal to x returns (lanes 0-31: x, x[l+32]; lanes 32-63: x[l-32], x), so
+// combining its two results gives every lane the value over lanes l and l ^ 32.
+__device__ inline float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// 16-byte LDS read / write
+__device__ inline u32x4 lds_read16(const FA_LDS uint8_t* p) {
+  return *reinterpret_cast<const FA_LDS u32x4*>(p);
+}
+__device__ inline void lds_write16(FA_LDS uint8_t* p, u32x4 v) {
+  *reinterpret_cast<FA_LDS u32x4*>(p) = v;
+}
+// transposing 8-byte LDS read (see header comment)
+__device__ inline u32x2 lds_read_tr16(const FA_LDS uint8_t* p) {
+  i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<FA_LDS i16x4*>(const_cast<FA_LDS uint8_t*>(p)));
+  return __builtin_bit_cast(u32x2, t);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16*l (lds_base wave-uniform).
+__device__ inline void global_to_lds16(const void* gptr, FA_LDS void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, lds_base, 16, 0, 0);
+}
+
+// XOR swizzle of 16-byte chunks inside a 16-bit-element tile row, so that
+// (a) 16 consecutive rows read at one logical chunk hit 16 distinct chunk slots and
+// (b) 4 consecutive rows read through the transposing load hit distinct 64-byte groups.
+template <int D> __device__ __host__ constexpr int chunk_swizzle(int row) {
+  if constexpr (D == 128) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else {
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  }
+}
+
+// byte offset of (row, logical 16-byte chunk) in a swizzled [rows][D] 16-bit tile
+template <int D> __device__ __host__ constexpr int tile_off(int row, int chunk) {
+  return row * (D * 2) + ((chunk ^ chunk_swizzle<D>(row)) << 4);
+}
+
+}  // namespace fa

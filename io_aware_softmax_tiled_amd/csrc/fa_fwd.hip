@@ -1,0 +1,496 @@
+// Forward pass of exact attention on gfx950: one workgroup per block of 128 query rows
+// of one (batch, head); key/value tiles of 64 rows stream through LDS while the
+// online-softmax state (running maximum, running denominator, unnormalised output)
+// stays in registers, so the N x N scores never reach HBM.
+//
+// Method: "[Review] From Online Softmax to Flash Attention", Algorithm FlashAttention
+// (Tiling) -- per key tile: local maximum, new running maximum, denominator rescaled
+// by e^{m_old - m_new} plus the tile's sum, output rescaled the same way plus the
+// tile's P V. "FlashAttention: Fast and Memory-Efficient Exact Attention with
+// IO-Awareness", Method: the same update in Br x Bc block form. Loop order: query
+// blocks outer (one per workgroup), key/value tiles inner, as in the review's
+// Thoughts section on FlashAttention-2.
+//
+// Choices made for CDNA4 (not taken from the pages):
+// * Scores are computed transposed, S^T = K Q^T, on 32x32x16 matrix cores, so each
+//   lane owns one query row: the row maximum and row sum are in-lane reductions plus
+//   one swap between the two 32-lane halves, and the output rescale is a per-lane
+//   scalar. K rows are read with bits 2 and 3 of the row index swapped, which makes
+//   every lane's 8 consecutive accumulator registers hold 8 consecutive keys: the
+//   packed P feeds the P V product as its B operand with no data movement.
+// * O^T = V^T P^T takes V^T through the transposing LDS read, so V is staged in LDS
+//   row-major exactly like K.
+// * K and V tiles go global -> LDS with the direct LDS load (no VGPR staging),
+//   double-buffered, into an XOR-swizzled layout; one barrier per tile.
+// * exp2 with scale*log2(e) folded into one FMA; the output is normalised once at the
+//   end (the pages normalise every step; the results are equal). The reference
+//   maximum used in the exponent is only raised when a tile's maximum exceeds it by
+//   more than 2^8 in the exponent, so most tiles skip the output rescale; the final
+//   division uses the same reference, so the result is unchanged.
+// * Causal masking is applied only on tiles that cross the diagonal, the key-padding
+//   bound or the end of the sequence; tiles past the diagonal or the padding are not
+//   visited at all, and 32-key halves that are fully masked for a wave are skipped.
+// * Workgroups are ordered heaviest-first for causal attention, and all query blocks
+//   of a head are placed on one XCD so its K/V tiles are shared in that XCD's L2.
+#include "fa_common.h"
+#include "fa_internal.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kBM = 128;   // query rows per workgroup (4 waves x 32)
+constexpr int kBN = 64;    // key rows per tile
+constexpr int kThreads = 256;
+
+// swap bits 2 and 3 of a row index in [0, 32)
+__device__ inline int kappa(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+struct WgPos {
+  int bh, mblk;
+};
+
+// blockIdx.x -> (head, query block): XCD-major, heaviest query block first.
+__device__ inline WgPos wg_position(int BH, int n_mblk, int heads_per_xcd) {
+  const int w = blockIdx.x;
+  const int xcd = w & 7;
+  const int slot = w >> 3;
+  const int hx = slot % heads_per_xcd;
+  const int mrev = slot / heads_per_xcd;
+  return {hx * 8 + xcd, n_mblk - 1 - mrev};
+}
+
+// ---------------------------------------------------------------------------------
+// 16-bit inputs (bf16 or f16)
+// ---------------------------------------------------------------------------------
+// 8 input elements (16 bytes of bf16 or f16) -> 8 fp16
+template <typename T> __device__ inline u32x4 to_f16x8(u32x4 x);
+template <> __device__ inline u32x4 to_f16x8<F16>(u32x4 x) { return x; }
+template <> __device__ inline u32x4 to_f16x8<BF16>(u32x4 x) {
+  return {bf16x2_to_f16x2(x[0]), bf16x2_to_f16x2(x[1]), bf16x2_to_f16x2(x[2]),
+          bf16x2_to_f16x2(x[3])};
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, 2) void fwd_kernel_16(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
+    int BH, int H, int N, float scale, float sl2, int causal,
+    const int* __restrict__ kv_len, int n_mblk, int heads_per_xcd) {
+  constexpr int kTileBytes = kBN * D * 2;              // one K or V tile
+  constexpr int kKC = D / 16;                          // 16-wide k-steps over head_dim
+  constexpr int kDB = D / 32;                          // 32-row blocks of O^T
+  constexpr int kKLoads = kTileBytes / 1024 / 4;       // direct K loads per wave per tile
+  constexpr int kCPR = D / 8;                          // 16-byte chunks per row
+  constexpr int kVChunks = kTileBytes / 16 / kThreads; // V chunks per thread per tile
+  // two buffers, as separate arrays so the compiler can tell the tile being read from
+  // the tile being filled by the direct loads
+  __shared__ __attribute__((aligned(1024))) uint8_t Kb0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t Kb1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vb0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vb1[kTileBytes];
+
+  const WgPos pos = wg_position(BH, n_mblk, heads_per_xcd);
+  if (pos.bh >= BH) return;
+  const int b = pos.bh / H;
+  const size_t head = (size_t)pos.bh * N * D;
+  const uint16_t* q = Q + head;
+  const uint16_t* k = K + head;
+  const uint16_t* v = V + head;
+
+  int kv_lim = N;
+  if (kv_len != nullptr) kv_lim = min(N, max(1, kv_len[b]));
+  const int m0 = pos.mblk * kBM;
+  const int kend = causal ? min(kv_lim, m0 + kBM) : kv_lim;
+  const int ntiles = (kend + kBN - 1) / kBN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int qi = lane & 31;
+  const int hh = lane >> 5;
+  const int wq0 = m0 + wave * 32;              // first query row of this wave
+  const int qrow = wq0 + qi;
+  const int qrow_c = min(qrow, N - 1);
+
+  // K tile t -> LDS by direct loads: each wave fills kKLoads 1 KB regions; lane l of a
+  // region fills its 16-byte slot l, so it fetches the chunk the swizzle puts there.
+  auto issue_k = [&](int t, FA_LDS uint8_t* kb) {
+    const int n0 = t * kBN;
+#pragma unroll
+    for (int j = 0; j < kKLoads; ++j) {
+      const int region = wave * kKLoads + j;
+      const int byte = region * 1024 + lane * 16;
+      const int row = byte / (D * 2);
+      const int pch = (byte % (D * 2)) >> 4;
+      const int lch = pch ^ chunk_swizzle<D>(row);
+      global_to_lds16(k + (size_t)min(n0 + row, N - 1) * D + lch * 8, kb + region * 1024);
+    }
+  };
+  // V tile t -> registers (coalesced 16-byte loads), later converted to fp16 into LDS
+  u32x4 vstage[kVChunks];
+  auto load_v = [&](int t) {
+    const int n0 = t * kBN;
+#pragma unroll
+    for (int j = 0; j < kVChunks; ++j) {
+      const int ci = tid + kThreads * j;
+      const int row = ci / kCPR, ch = ci % kCPR;
+      vstage[j] = *reinterpret_cast<const u32x4*>(v + (size_t)min(n0 + row, N - 1) * D + ch * 8);
+    }
+  };
+  auto store_v = [&](FA_LDS uint8_t* vb) {
+#pragma unroll
+    for (int j = 0; j < kVChunks; ++j) {
+      const int ci = tid + kThreads * j;
+      const int row = ci / kCPR, ch = ci % kCPR;
+      lds_write16(vb + tile_off<D>(row, ch), to_f16x8<T>(vstage[j]));
+    }
+  };
+
+  if (ntiles > 0) {
+    issue_k(0, (FA_LDS uint8_t*)Kb0);
+    load_v(0);
+  }
+
+  // Q fragment: B operand of S^T = K Q^T, lane (qi, hh) holds Q[qrow][16c + 8hh + 0..7]
+  u32x4 qf[kKC];
+#pragma unroll
+  for (int c = 0; c < kKC; ++c)
+    qf[c] = *reinterpret_cast<const u32x4*>(q + (size_t)qrow_c * D + 16 * c + 8 * hh);
+
+  f32x16 oacc[kDB];
+#pragma unroll
+  for (int i = 0; i < kDB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+
+  float m_ref = -INFINITY;  // reference maximum used in the exponent (raw score units)
+  float lsum = 0.f;         // this lane's half of the running denominator
+  const int krow_base = kappa(qi);
+  const int g = lane >> 4, gi = lane & 15;
+
+  if (ntiles > 0) store_v((FA_LDS uint8_t*)Vb0);
+
+  // one tile: publish it (barrier), start fetching the next one into the other buffer,
+  // then run the online-softmax update on this one
+  auto step = [&](int t, const FA_LDS uint8_t* Ks, const FA_LDS uint8_t* Vs,
+                  FA_LDS uint8_t* Kn, FA_LDS uint8_t* Vn) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const bool more = t + 1 < ntiles;
+    if (more) {
+      issue_k(t + 1, Kn);
+      load_v(t + 1);
+    }
+    const int n0 = t * kBN;
+    bool vis[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+      vis[sub] = (n0 + 32 * sub < kv_lim) && (!causal || n0 + 32 * sub <= wq0 + 31);
+    if (vis[0] || vis[1]) {
+      f32x16 sacc[2];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[sub][r] = 0.f;
+        if (vis[sub]) {
+          const int krow = sub * 32 + krow_base;
+#pragma unroll
+          for (int c = 0; c < kKC; ++c) {
+            const u32x4 a = lds_read16(Ks + tile_off<D>(krow, 2 * c + hh));
+            sacc[sub] = Mfma<T>::run(a, qf[c], sacc[sub]);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[sub][r] = -INFINITY;
+        }
+      }
+
+      // masks: only on tiles crossing the diagonal, the padding bound or the end
+      const bool need_mask = (n0 + kBN > kv_lim) || (causal && n0 + kBN - 1 > wq0);
+      if (need_mask) {
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = n0 + 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
+            const bool hide = key >= kv_lim || (causal && key > qrow);
+            sacc[sub][r] = hide ? -INFINITY : sacc[sub][r];
+          }
+      }
+
+      // row maximum of this tile (both halves of the wave hold the same query rows)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = max3f(mx, sacc[sub][r], sacc[sub][r + 1]);
+      mx = max_halves(mx);
+
+      // a row raises its reference maximum only when the exponent would exceed 2^8;
+      // the decision is per row, so each row's arithmetic depends on its own scores only
+      const bool grow = (mx - m_ref) * sl2 > 8.0f;
+      if (__any(grow)) {
+        const float m_new = grow ? mx : m_ref;
+        const float alpha = exp2_fast((m_ref - m_new) * sl2);  // 1 if kept, 0 from -inf
+        m_ref = m_new;
+        lsum *= alpha;
+#pragma unroll
+        for (int i = 0; i < kDB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+      }
+
+      // P = exp2(s*scale*log2e - m_ref*scale*log2e), rounded to fp16, and its row sum
+      const float nms = -m_ref * sl2;
+      uint32_t pk[2][8];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p0 = exp2_fast(fmaf(sacc[sub][2 * i], sl2, nms));
+          const float p1 = exp2_fast(fmaf(sacc[sub][2 * i + 1], sl2, nms));
+          pk[sub][i] = Mfma<F16>::pack(p0, p1);
+          lsum = Mfma<F16>::dot_ones(pk[sub][i], lsum);
+        }
+
+      // O^T += V^T P^T: four 16-key steps per tile
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (!vis[c >> 1]) continue;
+        const u32x4 bp = {pk[c >> 1][4 * (c & 1) + 0], pk[c >> 1][4 * (c & 1) + 1],
+                          pk[c >> 1][4 * (c & 1) + 2], pk[c >> 1][4 * (c & 1) + 3]};
+        const int vrow = 16 * c + 8 * hh + (gi >> 2);
+        const int inner = 8 * (gi & 1);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const int vch = db * 4 + 2 * (g & 1) + ((gi & 3) >> 1);
+          const u32x2 lo = lds_read_tr16(Vs + tile_off<D>(vrow, vch) + inner);
+          const u32x2 hi = lds_read_tr16(Vs + tile_off<D>(vrow + 4, vch) + inner);
+          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+          oacc[db] = Mfma<F16>::run(a, bp, oacc[db]);
+        }
+      }
+    }
+    if (more) store_v(Vn);
+  };
+
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, (const FA_LDS uint8_t*)Kb0, (const FA_LDS uint8_t*)Vb0, (FA_LDS uint8_t*)Kb1,
+         (FA_LDS uint8_t*)Vb1);
+    if (t + 1 < ntiles)
+      step(t + 1, (const FA_LDS uint8_t*)Kb1, (const FA_LDS uint8_t*)Vb1, (FA_LDS uint8_t*)Kb0,
+           (FA_LDS uint8_t*)Vb0);
+  }
+
+  // epilogue: O = O_acc / l, LSE = scale*m_ref + ln(l)
+  const float ltot = sum_halves(lsum);
+  if (qrow < N) {
+    const float inv = 1.0f / ltot;
+    float* orow = O + head + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 val = {oacc[db][4 * a4 + 0] * inv, oacc[db][4 * a4 + 1] * inv,
+                           oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv};
+        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * a4 + 4 * hh) = val;
+      }
+    if (hh == 0) LSE[(size_t)pos.bh * N + qrow] = m_ref * scale + log2_fast(ltot) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// fp32 inputs: the same S^T / O^T orientation on the 32x32x2 fp32 matrix cores.
+// ---------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void fwd_kernel_f32(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, int BH, int H, int N, float scale,
+    float sl2, int causal, const int* __restrict__ kv_len, int n_mblk, int heads_per_xcd) {
+  constexpr int kLd = D + 4;                   // padded row (floats)
+  constexpr int kDB = D / 32;
+  __shared__ __attribute__((aligned(16))) float Ks[kBN * kLd];
+  __shared__ __attribute__((aligned(16))) float Vs[kBN * kLd];
+
+  const WgPos pos = wg_position(BH, n_mblk, heads_per_xcd);
+  if (pos.bh >= BH) return;
+  const int b = pos.bh / H;
+  const size_t head = (size_t)pos.bh * N * D;
+  const float* q = Q + head;
+  const float* k = K + head;
+  const float* v = V + head;
+  int kv_lim = N;
+  if (kv_len != nullptr) kv_lim = min(N, max(1, kv_len[b]));
+  const int m0 = pos.mblk * kBM;
+  const int kend = causal ? min(kv_lim, m0 + kBM) : kv_lim;
+  const int ntiles = (kend + kBN - 1) / kBN;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int qi = lane & 31;
+  const int hh = lane >> 5;
+  const int wq0 = m0 + wave * 32;
+  const int qrow = wq0 + qi;
+  const int qrow_c = min(qrow, N - 1);
+
+  // Q fragment: lane (qi, hh) holds Q[qrow][2c + hh], c = 0..D/2-1
+  float qf[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) qf[c] = q[(size_t)qrow_c * D + 2 * c + hh];
+
+  f32x16 oacc[kDB];
+#pragma unroll
+  for (int i = 0; i < kDB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+  float m_ref = -INFINITY;
+  float lsum = 0.f;
+  const int krow_base = kappa(qi);
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int n0 = t * kBN;
+    __syncthreads();
+    for (int e = threadIdx.x; e < kBN * D / 4; e += kThreads) {
+      const int row = e / (D / 4), c4 = e % (D / 4);
+      const size_t goff = (size_t)min(n0 + row, N - 1) * D + 4 * c4;
+      const f32x4 kv4 = *reinterpret_cast<const f32x4*>(k + goff);
+      const f32x4 vv4 = *reinterpret_cast<const f32x4*>(v + goff);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        Ks[row * kLd + 4 * c4 + j] = kv4[j];
+        Vs[row * kLd + 4 * c4 + j] = vv4[j];
+      }
+    }
+    __syncthreads();
+
+    bool vis[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+      vis[sub] = (n0 + 32 * sub < kv_lim) && (!causal || n0 + 32 * sub <= wq0 + 31);
+    if (!vis[0] && !vis[1]) continue;
+
+    f32x16 sacc[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[sub][r] = 0.f;
+      if (vis[sub]) {
+        const float* krow = Ks + (sub * 32 + krow_base) * kLd;
+#pragma unroll
+        for (int c = 0; c < D / 2; ++c)
+          sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * c + hh], qf[c], sacc[sub],
+                                                           0, 0, 0);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[sub][r] = -INFINITY;
+      }
+    }
+    const bool need_mask = (n0 + kBN > kv_lim) || (causal && n0 + kBN - 1 > wq0);
+    if (need_mask) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = n0 + 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
+          const bool hide = key >= kv_lim || (causal && key > qrow);
+          sacc[sub][r] = hide ? -INFINITY : sacc[sub][r];
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = max3f(mx, sacc[sub][r], sacc[sub][r + 1]);
+    mx = max_halves(mx);
+    const bool grow = (mx - m_ref) * sl2 > 8.0f;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_ref;
+      const float alpha = exp2_fast((m_ref - m_new) * sl2);
+      m_ref = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < kDB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+    }
+    const float nms = -m_ref * sl2;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sacc[sub][r] = exp2_fast(fmaf(sacc[sub][r], sl2, nms));
+        lsum += sacc[sub][r];
+      }
+    // O^T += V^T P^T, one key per half-wave per instruction
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      if (!vis[sub]) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * kLd + db * 32 + qi],
+                                                          sacc[sub][r], oacc[db], 0, 0, 0);
+      }
+    }
+  }
+
+  const float ltot = sum_halves(lsum);
+  if (qrow < N) {
+    const float inv = 1.0f / ltot;
+    float* orow = O + head + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 val = {oacc[db][4 * a4 + 0] * inv, oacc[db][4 * a4 + 1] * inv,
+                           oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv};
+        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * a4 + 4 * hh) = val;
+      }
+    if (hh == 0) LSE[(size_t)pos.bh * N + qrow] = m_ref * scale + __logf(ltot);
+  }
+}
+
+}  // namespace
+
+FwdGrid fwd_grid(int B, int H, int N) {
+  FwdGrid g;
+  g.n_mblk = (N + kBM - 1) / kBM;
+  g.heads_per_xcd = (B * H + 7) / 8;
+  g.blocks = 8 * g.heads_per_xcd * g.n_mblk;
+  return g;
+}
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+  const FwdGrid g = fwd_grid(a.B, a.H, a.N);
+  const auto* q16 = static_cast<const uint16_t*>(a.q);
+  const auto* k16 = static_cast<const uint16_t*>(a.k);
+  const auto* v16 = static_cast<const uint16_t*>(a.v);
+  const float sl2 = a.scale * kLog2e;
+  const int BH = a.B * a.H;
+#define FA_LAUNCH16(TAG, DIM)                                                              \
+  hipLaunchKernelGGL((fwd_kernel_16<TAG, DIM>), dim3(g.blocks), dim3(kThreads), 0, stream, \
+                     q16, k16, v16, a.o, a.lse, BH, a.H, a.N, a.scale, sl2, a.causal,      \
+                     a.kv_len, g.n_mblk, g.heads_per_xcd)
+#define FA_LAUNCH32(DIM)                                                                  \
+  hipLaunchKernelGGL((fwd_kernel_f32<DIM>), dim3(g.blocks), dim3(kThreads), 0, stream,    \
+                     static_cast<const float*>(a.q), static_cast<const float*>(a.k),       \
+                     static_cast<const float*>(a.v), a.o, a.lse, BH, a.H, a.N, a.scale, sl2, \
+                     a.causal, a.kv_len, g.n_mblk, g.heads_per_xcd)
+  if (a.dtype == kDtypeBF16) {
+    if (a.d == 64) FA_LAUNCH16(BF16, 64); else FA_LAUNCH16(BF16, 128);
+  } else if (a.dtype == kDtypeF16) {
+    if (a.d == 64) FA_LAUNCH16(F16, 64); else FA_LAUNCH16(F16, 128);
+  } else {
+    if (a.d == 64) FA_LAUNCH32(64); else FA_LAUNCH32(128);
+  }
+#undef FA_LAUNCH16
+#undef FA_LAUNCH32
+  return hipGetLastError();
+}
+
+}  // namespace fa

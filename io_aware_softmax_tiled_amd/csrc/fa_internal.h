@@ -1,0 +1,56 @@
+// Host-side interface between the C ABI layer (fa_api.cpp) and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBF16 = 1;
+constexpr int kDtypeF16 = 2;
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;
+  float* lse;
+  int B, H, N, d;
+  float scale;
+  int causal;
+  int dtype;
+  const int* kv_len;
+};
+
+struct FwdGrid {
+  int n_mblk;
+  int heads_per_xcd;
+  int blocks;
+};
+
+FwdGrid fwd_grid(int B, int H, int N);
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* o;
+  const void* dout;
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  int B, H, N, d;
+  float scale;
+  int causal;
+  int dtype;
+  const int* kv_len;
+  float* delta;  // workspace: D_i = rowsum(dO * O), [B,H,N]
+};
+
+size_t bwd_workspace_bytes(int B, int H, int N, int d);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,135 @@
+"""The C ABI library on the CPU: it loads, exports every symbol include/fa.h declares,
+and rejects invalid arguments on the host with the documented codes before touching the
+GPU. No call here launches a kernel (no GPU is needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import io_aware_softmax_tiled_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EWORKSPACE, FA_EHIP = 0, 1, 2, 3, 4
+P = 0x7f0000001000  # a 4 KiB-aligned fake device address: never dereferenced on error
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"FA_API\s+[\w\s\*]+?\b(fa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.lib_path()):
+        pytest.fail("libfa_mi355x.so is not built (python -m io_aware_softmax_tiled_amd.build)")
+    return fa.load_library()
+
+
+def test_header_declares_the_api():
+    assert declared_symbols() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd",
+                                  "fa_last_error", "fa_status_str", "fa_version"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)", out))
+    for name in declared_symbols():
+        assert name in exported, f"{name} not exported"
+        assert hasattr(lib, name)
+    # nothing else with the public prefix leaks out
+    assert {s for s in exported if s.startswith("fa_")} == set(declared_symbols())
+
+
+def test_status_strings_and_version(lib):
+    for code in range(5):
+        assert fa.fa_status_str(code).startswith("FA_")
+    assert fa.fa_status_str(99) == "unknown status"
+    assert fa.fa_version() == 100
+    assert fa.fa_last_error() == ""
+
+
+def _fwd(lib, q=P, k=P + 0x100000, v=P + 0x200000, o=P + 0x300000, lse=P + 0x400000,
+         B=1, H=1, N=64, d=64, scale=0.125, causal=0, dtype=1, kv=None):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, kv, None)
+
+
+def _bwd(lib, B=1, H=1, N=64, d=64, scale=0.125, dtype=1, ws=P + 0x900000, ws_bytes=None,
+         **over):
+    ptrs = dict(q=P, k=P + 0x100000, v=P + 0x200000, o=P + 0x300000, dout=P + 0x400000,
+                lse=P + 0x500000, dq=P + 0x600000, dk=P + 0x700000, dv=P + 0x800000)
+    ptrs.update(over)
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_size(B, H, N, d)
+    return lib.fa_bwd(ptrs["q"], ptrs["k"], ptrs["v"], ptrs["o"], ptrs["dout"], ptrs["lse"],
+                      ptrs["dq"], ptrs["dk"], ptrs["dv"], B, H, N, d, scale, 0, dtype, None,
+                      ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), FA_EINVAL),
+    (dict(lse=None), FA_EINVAL),
+    (dict(d=96), FA_EUNSUPPORTED),
+    (dict(d=32), FA_EUNSUPPORTED),
+    (dict(dtype=7), FA_EUNSUPPORTED),
+    (dict(N=-1), FA_EINVAL),
+    (dict(B=-2), FA_EINVAL),
+    (dict(scale=0.0), FA_EINVAL),
+    (dict(scale=-1.0), FA_EINVAL),
+    (dict(scale=float("inf")), FA_EINVAL),
+    (dict(scale=float("nan")), FA_EINVAL),
+    (dict(N=(1 << 22) + 1), FA_EINVAL),
+    (dict(q=P + 8), FA_EINVAL),            # misaligned
+    (dict(o=P + 4), FA_EINVAL),
+    (dict(lse=P + 0x400002), FA_EINVAL),
+    (dict(kv=P + 0x500002), FA_EINVAL),
+    (dict(o=P), FA_EINVAL),                # output overlaps q
+    (dict(lse=P + 0x300000 + 64), FA_EINVAL),  # lse inside o
+])
+def test_fwd_rejects_before_launch(lib, kw, code):
+    assert _fwd(lib, **kw) == code
+    assert fa.fa_last_error() != ""
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=0, q=None)])
+def test_fwd_empty_is_noop(lib, kw):
+    assert _fwd(lib, **kw) == FA_OK
+
+
+def test_workspace_size(lib):
+    assert fa.fa_bwd_workspace_size(2, 3, 100, 64) == ((2 * 3 * 100 * 4 + 255) // 256) * 256
+    assert fa.fa_bwd_workspace_size(0, 3, 100, 64) == 0
+    assert fa.fa_bwd_workspace_size(8, 16, 512, 64) % 256 == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), FA_EUNSUPPORTED),      # no fp32 backward
+    (dict(d=80), FA_EUNSUPPORTED),
+    (dict(dq=None), FA_EINVAL),
+    (dict(ws=None), FA_EWORKSPACE),
+    (dict(ws_bytes=16), FA_EWORKSPACE),
+    (dict(ws=P + 0x900000 + 16), FA_EINVAL),   # workspace not 256-aligned
+    (dict(dk=P + 0x100000), FA_EINVAL),        # dk overlaps k
+    (dict(dv=P + 0x600000), FA_EINVAL),        # dv overlaps dq
+    (dict(lse=P + 0x500002), FA_EINVAL),
+    (dict(scale=0.0), FA_EINVAL),
+])
+def test_bwd_rejects_before_launch(lib, kw, code):
+    assert _bwd(lib, **kw) == code
+    assert fa.fa_last_error() != ""
+
+
+def test_bwd_empty_is_noop(lib):
+    assert _bwd(lib, N=0) == FA_OK
+    assert _bwd(lib, B=0, ws=None, ws_bytes=0) == FA_OK
+
+
+def test_python_binding_requires_gpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, q, q)
