@@ -151,7 +151,7 @@ def main():
     bwd_tf = bwd_f / (bwd_ms * 1e-3) / 1e12
     # the dominant call of the step; its kernels: fwd = one kernel, bwd = pre + main
     if bwd_ms >= fwd_ms:
-        dom = {"kernel": "fa_bwd (bwd_pre_kernel + bwd_main_kernel)", "ms": bwd_ms,
+        dom = {"kernel": "fa_bwd (bwd_pre_kernel + bwd_dkdv_kernel + bwd_dq_kernel)", "ms": bwd_ms,
                "flops": bwd_f, "traffic_key": "fa_bwd"}
     else:
         dom = {"kernel": "fwd_kernel_16", "ms": fwd_ms, "flops": fwd_f,

@@ -95,8 +95,9 @@ FA_API size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  * probabilities are recomputed on chip from q, k and lse, tile by tile.
  * workspace: device memory of at least fa_bwd_workspace_size(B,H,N,d) bytes,
  * 256-byte aligned, owned by the caller, contents on entry irrelevant.
- * dq is accumulated with float32 atomics, so its last bits may differ from run
- * to run; dk and dv are deterministic. dtype must be FA_BF16 or FA_F16 (an FA_F32
+ * Three kernels run in order on `stream`: D = rowsum(dout*o) into the workspace,
+ * then dk/dv (keys outer), then dq (queries outer); each output is written exactly
+ * once, so results are deterministic. dtype must be FA_BF16 or FA_F16 (an FA_F32
  * backward is not provided: FA_EUNSUPPORTED).
  */
 FA_API int fa_bwd(const void* q, const void* k, const void* v, const float* o,

@@ -8,14 +8,20 @@
 // them): dV = P^T dO, dP = dO V^T, D_i = sum_k dO_ik O_ik, dS = P * (dP - D),
 // dQ = scale * dS K, dK = scale * dS^T Q.
 //
-// Kernels:
-// 1. bwd_pre: D_i = rowsum(dO * O) into the workspace, and dq := 0.
-// 2. bwd_main: one workgroup per 128 keys of one (batch, head), 32 keys per wave. The
-//    loop runs over 32-query tiles (for causal attention, from the first tile that
-//    reaches the block's keys). Per tile each wave recomputes S = Q K^T and
-//    dP = dO V^T with keys on lanes, forms P and dS in registers, accumulates
-//    dV^T += dO^T P and dK^T += Q^T dS in registers, publishes dS^T through LDS, and
-//    then contributes dQ = dS K for the tile, added to dq with fp32 atomics.
+// Kernels (no atomics; every output is written once, so all of them are deterministic):
+// 1. bwd_pre: D_i = rowsum(dO * O) into the workspace.
+// 2. bwd_dkdv: one workgroup per 128 keys of one (batch, head), 32 keys per wave, keys
+//    on lanes. It loops over 32-query tiles (causal: from the block's diagonal on),
+//    recomputes S = Q K^T and dP = dO V^T, forms P and dS in registers, and accumulates
+//    dV^T += dO^T P and dK^T += Q^T dS in registers (dO^T and Q^T through the
+//    transposing LDS read). Q/dO tiles are prefetched one tile ahead and
+//    double-buffered: one barrier per tile.
+// 3. bwd_dq: one workgroup per 128 queries, 32 per wave, queries on lanes -- the
+//    forward kernel's layout. Per 64-key tile it recomputes S^T = K Q^T and
+//    dP^T = V dO^T, forms dS^T in registers and accumulates dQ^T += K^T dS^T (K^T
+//    through the transposing LDS read). Recomputing S and dP here costs two extra
+//    products per score, in exchange for no fp32 atomics on dq and no dS round trip
+//    through LDS.
 //
 // Precision: every matrix-core product runs in fp16 with fp32 accumulation. bf16
 // inputs are converted to fp16 when staged (exact for magnitudes in the fp16 normal
@@ -29,18 +35,6 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBK = 128;  // keys per workgroup
-constexpr int kBQ = 32;   // queries per iteration
-
-__device__ inline int kappa(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
-
-// 8 input elements (16 bytes of bf16 or f16) -> 8 fp16 (16 bytes)
-template <typename T> __device__ inline u32x4 to_f16x8(u32x4 x);
-template <> __device__ inline u32x4 to_f16x8<F16>(u32x4 x) { return x; }
-template <> __device__ inline u32x4 to_f16x8<BF16>(u32x4 x) {
-  return {bf16x2_to_f16x2(x[0]), bf16x2_to_f16x2(x[1]), bf16x2_to_f16x2(x[2]),
-          bf16x2_to_f16x2(x[3])};
-}
 
 template <typename T> __device__ inline float to_f32(uint16_t x);
 template <> __device__ inline float to_f32<BF16>(uint16_t x) {
@@ -50,19 +44,13 @@ template <> __device__ inline float to_f32<F16>(uint16_t x) {
   return (float)__builtin_bit_cast(_Float16, x);
 }
 
-// byte offset in the dS^T tile [128 keys][32 queries] fp16 (64-byte rows): the
-// 16-byte chunk index is XORed with bits 2..3 of the row.
-__device__ inline int dst_off(int row, int byte) {
-  return row * 64 + (byte ^ (((row >> 2) & 3) << 4));
-}
-
 // ---------------------------------------------------------------------------------
-// 1. D = rowsum(dO * O), dq = 0. One thread per 8 elements; D/8 threads per row.
+// 1. D = rowsum(dO * O). One thread per 8 elements; D/8 threads per row.
 // ---------------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ O, float* __restrict__ delta,
-    float* __restrict__ dQ, size_t rows) {
+    size_t rows) {
   constexpr int kTPR = D / 8;
   const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
   const size_t row = idx / kTPR;
@@ -80,34 +68,6 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
       s = fmaf(lo, olo, s);
       s = fmaf(hi, ohi, s);
     }
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(dQ + idx * 8) = z;
-    *reinterpret_cast<f32x4*>(dQ + idx * 8 + 4) = z;
-  }
-#pragma unroll
-  for (int off = kTPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kTPR);
-  if (row < rows && (threadIdx.x % kTPR) == 0) delta[row] = s;
-}
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel_f32(
-    const float* __restrict__ dO, const float* __restrict__ O, float* __restrict__ delta,
-    float* __restrict__ dQ, size_t rows) {
-  constexpr int kTPR = D / 8;
-  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  const size_t row = idx / kTPR;
-  float s = 0.f;
-  if (row < rows) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const f32x4 g = *reinterpret_cast<const f32x4*>(dO + idx * 8 + 4 * j);
-      const f32x4 o = *reinterpret_cast<const f32x4*>(O + idx * 8 + 4 * j);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s = fmaf(g[e], o[e], s);
-    }
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(dQ + idx * 8) = z;
-    *reinterpret_cast<f32x4*>(dQ + idx * 8 + 4) = z;
   }
 #pragma unroll
   for (int off = kTPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kTPR);
@@ -115,32 +75,34 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel_f32(
 }
 
 // ---------------------------------------------------------------------------------
-// 2. main backward kernel, 16-bit inputs
+// 2. dK, dV: keys on lanes
 // ---------------------------------------------------------------------------------
+constexpr int kBK = 128;  // keys per workgroup
+constexpr int kBQ = 32;   // queries per tile
+
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ delta, float* __restrict__ dQ,
-    float* __restrict__ dK, float* __restrict__ dV, int BH, int H, int N, float scale,
-    float sl2, int causal, const int* __restrict__ kv_len, int n_kblk, int heads_per_xcd) {
+    const float* __restrict__ LSE, const float* __restrict__ delta, float* __restrict__ dK,
+    float* __restrict__ dV, int BH, int H, int N, float scale, float sl2, int causal,
+    const int* __restrict__ kv_len, int n_kblk, int heads_per_xcd) {
   constexpr int kKC = D / 16;
   constexpr int kDB = D / 32;
-  constexpr int kCPR = D / 8;  // 16-byte chunks per row
-  __shared__ __attribute__((aligned(1024))) uint8_t Ks[kBK * D * 2];
-  __shared__ __attribute__((aligned(1024))) uint8_t Qs[kBQ * D * 2];
-  __shared__ __attribute__((aligned(1024))) uint8_t dOs[kBQ * D * 2];
-  __shared__ __attribute__((aligned(1024))) uint8_t dSt[kBK * kBQ * 2];
-  __shared__ __attribute__((aligned(16))) float lse_s[kBQ];
-  __shared__ __attribute__((aligned(16))) float dlt_s[kBQ];
+  constexpr int kCPR = D / 8;                        // 16-byte chunks per row
+  constexpr int kTile = kBQ * D * 2;                 // one Q or dO tile (fp16), bytes
+  constexpr int kSC = kTile / 16 / kThreads;         // staged chunks per thread per tensor
+  __shared__ __attribute__((aligned(1024))) uint8_t Qb0[kTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t Qb1[kTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t Ob0[kTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t Ob1[kTile];
+  __shared__ __attribute__((aligned(16))) float St0[2 * kBQ];  // LSE*log2(e), then D
+  __shared__ __attribute__((aligned(16))) float St1[2 * kBQ];
 
-  // workgroup -> (head, key block): XCD-major; key block 0 (the most query tiles
-  // under a causal mask) first
-  const int w = blockIdx.x;
-  const int xcd = w & 7, slot = w >> 3;
-  const int bh = (slot % heads_per_xcd) * 8 + xcd;
-  const int kblk = slot / heads_per_xcd;
-  if (bh >= BH || kblk >= n_kblk) return;
+  const WgPos pos = wg_position(heads_per_xcd);
+  const int kblk = pos.blk;  // key block 0 has the most query tiles under a causal mask
+  if (pos.bh >= BH || kblk >= n_kblk) return;
+  const int bh = pos.bh;
   const int b = bh / H;
   const size_t head = (size_t)bh * N * D;
   int kv_lim = N;
@@ -168,13 +130,44 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(
     return;
   }
 
-  // K block -> LDS (fp16, swizzled rows): B operand source of dQ = dS K
-  for (int ci = tid; ci < kBK * kCPR; ci += kThreads) {
-    const int row = ci / kCPR, ch = ci % kCPR;
-    const size_t goff = head + (size_t)min(k0 + row, N - 1) * D + ch * 8;
-    lds_write16((FA_LDS uint8_t*)Ks + tile_off<D>(row, ch),
-                to_f16x8<T>(*reinterpret_cast<const u32x4*>(K + goff)));
-  }
+  const int nq = (N + kBQ - 1) / kBQ;
+  const int i0 = causal ? k0 / kBQ : 0;
+
+  // staging of query tile `it` through registers (coalesced 16-byte loads)
+  u32x4 qs[kSC], os[kSC];
+  float s_lse = 0.f, s_dlt = 0.f;
+  auto load_tile = [&](int it) {
+    const int q0 = it * kBQ;
+#pragma unroll
+    for (int j = 0; j < kSC; ++j) {
+      const int ci = tid + kThreads * j;
+      const int row = ci / kCPR, ch = ci % kCPR;
+      const size_t goff = head + (size_t)min(q0 + row, N - 1) * D + ch * 8;
+      qs[j] = *reinterpret_cast<const u32x4*>(Q + goff);
+      os[j] = *reinterpret_cast<const u32x4*>(dO + goff);
+    }
+    if (tid < kBQ) {
+      const size_t r = (size_t)bh * N + min(q0 + tid, N - 1);
+      s_lse = LSE[r] * kLog2e;
+      s_dlt = delta[r];
+    }
+  };
+  auto store_tile = [&](FA_LDS uint8_t* qb, FA_LDS uint8_t* ob, FA_LDS float* st) {
+#pragma unroll
+    for (int j = 0; j < kSC; ++j) {
+      const int ci = tid + kThreads * j;
+      const int row = ci / kCPR, ch = ci % kCPR;
+      lds_write16(qb + tile_off<D>(row, ch), to_f16x8<T>(qs[j]));
+      lds_write16(ob + tile_off<D>(row, ch), to_f16x8<T>(os[j]));
+    }
+    if (tid < kBQ) {
+      st[tid] = s_lse;
+      st[kBQ + tid] = s_dlt;
+    }
+  };
+
+  if (i0 < nq) load_tile(i0);
+
   // this lane's key row of K and V as B operands (fp16): [key][16c + 8hh + 0..7]
   u32x4 kf[kKC], vf[kKC];
   {
@@ -185,7 +178,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(
       vf[c] = to_f16x8<T>(*reinterpret_cast<const u32x4*>(V + roff + 16 * c + 8 * hh));
     }
   }
-
   f32x16 dkacc[kDB], dvacc[kDB];
 #pragma unroll
   for (int i = 0; i < kDB; ++i)
@@ -194,34 +186,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(
       dkacc[i][r] = 0.f;
       dvacc[i][r] = 0.f;
     }
-
   const bool wave_dead = kw0 >= kv_lim;
-  const int nq = (N + kBQ - 1) / kBQ;
-  const int i0 = causal ? k0 / kBQ : 0;
   const int arow = kappa(li);  // A-operand row (query) read by this lane
-  const FA_LDS uint8_t* Qsl = (const FA_LDS uint8_t*)Qs;
-  const FA_LDS uint8_t* dOsl = (const FA_LDS uint8_t*)dOs;
-  const FA_LDS uint8_t* Ksl = (const FA_LDS uint8_t*)Ks;
-  FA_LDS uint8_t* dStl = (FA_LDS uint8_t*)dSt;
 
-  for (int it = i0; it < nq; ++it) {
-    const int q0 = it * kBQ;
-    // stage Q and dO tiles (fp16), the LSE (log2 units) and D of the tile
-    for (int ci = tid; ci < kBQ * kCPR; ci += kThreads) {
-      const int row = ci / kCPR, ch = ci % kCPR;
-      const size_t goff = head + (size_t)min(q0 + row, N - 1) * D + ch * 8;
-      lds_write16((FA_LDS uint8_t*)Qs + tile_off<D>(row, ch),
-                  to_f16x8<T>(*reinterpret_cast<const u32x4*>(Q + goff)));
-      lds_write16((FA_LDS uint8_t*)dOs + tile_off<D>(row, ch),
-                  to_f16x8<T>(*reinterpret_cast<const u32x4*>(dO + goff)));
-    }
-    if (tid < kBQ) {
-      const size_t r = (size_t)bh * N + min(q0 + tid, N - 1);
-      lse_s[tid] = LSE[r] * kLog2e;
-      dlt_s[tid] = delta[r];
-    }
+  if (i0 < nq) store_tile((FA_LDS uint8_t*)Qb0, (FA_LDS uint8_t*)Ob0, (FA_LDS float*)St0);
+
+  auto step = [&](int it, const FA_LDS uint8_t* Qc, const FA_LDS uint8_t* Oc,
+                  const FA_LDS float* Stc, FA_LDS uint8_t* Qn, FA_LDS uint8_t* On,
+                  FA_LDS float* Stn) {
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
+    const bool more = it + 1 < nq;
+    if (more) load_tile(it + 1);
+    const int q0 = it * kBQ;
     const bool active = !wave_dead && !(causal && kw0 > q0 + kBQ - 1);
     if (active) {
       f32x16 s, dp;
@@ -233,19 +210,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(
 #pragma unroll
       for (int c = 0; c < kKC; ++c) {
         const int off = tile_off<D>(arow, 2 * c + hh);
-        s = Mfma<F16>::run(lds_read16(Qsl + off), kf[c], s);
-        dp = Mfma<F16>::run(lds_read16(dOsl + off), vf[c], dp);
+        s = Mfma<F16>::run(lds_read16(Qc + off), kf[c], s);
+        dp = Mfma<F16>::run(lds_read16(Oc + off), vf[c], dp);
       }
       // lane (key, hh), register r <-> query q0 + 16*(r/8) + 8*hh + r%8
-      const bool need_mask = (causal && kw0 + 31 > q0) || (q0 + kBQ > N) || (kw0 + 32 > kv_lim);
+      const bool need_mask =
+          (causal && kw0 + 31 > q0) || (q0 + kBQ > N) || (kw0 + 32 > kv_lim);
       uint32_t pp[8], dsp[8];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int qb = 16 * c + 8 * hh;
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(&lse_s[qb]);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(&lse_s[qb + 4]);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&dlt_s[qb]);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&dlt_s[qb + 4]);
+        const f32x4 l0 = *reinterpret_cast<const FA_LDS f32x4*>(&Stc[qb]);
+        const f32x4 l1 = *reinterpret_cast<const FA_LDS f32x4*>(&Stc[qb + 4]);
+        const f32x4 d0 = *reinterpret_cast<const FA_LDS f32x4*>(&Stc[kBQ + qb]);
+        const f32x4 d1 = *reinterpret_cast<const FA_LDS f32x4*>(&Stc[kBQ + qb + 4]);
         float p[8], ds[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -277,60 +255,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
           const int ch = db * 4 + 2 * (g & 1) + ((gi & 3) >> 1);
-          const u32x2 a0 = lds_read_tr16(dOsl + tile_off<D>(trow, ch) + inner);
-          const u32x2 a1 = lds_read_tr16(dOsl + tile_off<D>(trow + 4, ch) + inner);
+          const u32x2 a0 = lds_read_tr16(Oc + tile_off<D>(trow, ch) + inner);
+          const u32x2 a1 = lds_read_tr16(Oc + tile_off<D>(trow + 4, ch) + inner);
           dvacc[db] = Mfma<F16>::run(u32x4{a0[0], a0[1], a1[0], a1[1]}, bp, dvacc[db]);
-          const u32x2 b0 = lds_read_tr16(Qsl + tile_off<D>(trow, ch) + inner);
-          const u32x2 b1 = lds_read_tr16(Qsl + tile_off<D>(trow + 4, ch) + inner);
+          const u32x2 b0 = lds_read_tr16(Qc + tile_off<D>(trow, ch) + inner);
+          const u32x2 b1 = lds_read_tr16(Qc + tile_off<D>(trow + 4, ch) + inner);
           dkacc[db] = Mfma<F16>::run(u32x4{b0[0], b0[1], b1[0], b1[1]}, bs, dkacc[db]);
         }
       }
-      // publish dS^T: row = key (block-local), queries 16c + 8hh + 0..7
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        lds_write16(dStl + dst_off(32 * wave + li, 32 * c + 16 * hh),
-                    u32x4{dsp[4 * c], dsp[4 * c + 1], dsp[4 * c + 2], dsp[4 * c + 3]});
-    } else {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int c = 0; c < 2; ++c) lds_write16(dStl + dst_off(32 * wave + li, 32 * c + 16 * hh), z);
     }
-    __syncthreads();
+    if (more) store_tile(Qn, On, Stn);
+  };
 
-    // dQ[q0 .. q0+31][d-block] += scale * dS K over this block's keys
-    {
-      const int db = wave % kDB;
-      const int nparts = 4 / kDB;              // waves sharing one d-block
-      const int part = wave / kDB;
-      const int kpp = kBK / nparts;            // keys per part
-      const bool any_live = !(causal && k0 + part * kpp > q0 + kBQ - 1) && (k0 + part * kpp < kv_lim);
-      if (any_live) {
-        f32x16 acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-        const int dch = db * 4 + 2 * (g & 1) + ((gi & 3) >> 1);
-        const int sbyte = 32 * (g & 1) + 8 * (gi & 3);
-        const int kinner = 8 * (gi & 1);
-#pragma unroll
-        for (int c = 0; c < kpp / 16; ++c) {
-          const int krow = part * kpp + 16 * c + 8 * hh + (gi >> 2);
-          const u32x2 a0 = lds_read_tr16(dStl + dst_off(krow, sbyte));
-          const u32x2 a1 = lds_read_tr16(dStl + dst_off(krow + 4, sbyte));
-          const u32x2 b0 = lds_read_tr16(Ksl + tile_off<D>(krow, dch) + kinner);
-          const u32x2 b1 = lds_read_tr16(Ksl + tile_off<D>(krow + 4, dch) + kinner);
-          acc = Mfma<F16>::run(u32x4{a0[0], a0[1], a1[0], a1[1]}, u32x4{b0[0], b0[1], b1[0], b1[1]},
-                               acc);
-        }
-        // lane (d = 32db + li, hh), register r <-> query q0 + 8*(r/4) + 4*hh + r%4
-        float* dqb = dQ + head + 32 * db + li;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qq = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (qq < N) unsafeAtomicAdd(dqb + (size_t)qq * D, scale * acc[r]);
-        }
-      }
-    }
-    __syncthreads();
+  for (int it = i0; it < nq; it += 2) {
+    step(it, (const FA_LDS uint8_t*)Qb0, (const FA_LDS uint8_t*)Ob0, (const FA_LDS float*)St0,
+         (FA_LDS uint8_t*)Qb1, (FA_LDS uint8_t*)Ob1, (FA_LDS float*)St1);
+    if (it + 1 < nq)
+      step(it + 1, (const FA_LDS uint8_t*)Qb1, (const FA_LDS uint8_t*)Ob1,
+           (const FA_LDS float*)St1, (FA_LDS uint8_t*)Qb0, (FA_LDS uint8_t*)Ob0,
+           (FA_LDS float*)St0);
   }
 
   // dK = scale * dK_acc, dV = dV_acc: lane (key, hh), register r <-> d = 32db + 8(r/4) + 4hh + r%4
@@ -352,6 +295,177 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------
+// 3. dQ: queries on lanes (the forward kernel's layout)
+// ---------------------------------------------------------------------------------
+constexpr int kBM = 128;  // queries per workgroup
+constexpr int kBN = 64;   // keys per tile
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ delta, float* __restrict__ dQ,
+    int BH, int H, int N, float scale, float sl2, int causal,
+    const int* __restrict__ kv_len, int n_mblk, int heads_per_xcd) {
+  constexpr int kKC = D / 16;
+  constexpr int kDB = D / 32;
+  constexpr int kCPR = D / 8;
+  constexpr int kTile = kBN * D * 2;                 // one K or V tile (fp16), bytes
+  constexpr int kSC = kTile / 16 / kThreads;         // staged chunks per thread per tensor
+  __shared__ __attribute__((aligned(1024))) uint8_t Kb0[kTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t Kb1[kTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vb0[kTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vb1[kTile];
+
+  const WgPos pos = wg_position(heads_per_xcd);
+  if (pos.bh >= BH) return;
+  const int mblk = n_mblk - 1 - pos.blk;  // heaviest query block first
+  const int bh = pos.bh;
+  const int b = bh / H;
+  const size_t head = (size_t)bh * N * D;
+  int kv_lim = N;
+  if (kv_len != nullptr) kv_lim = min(N, max(1, kv_len[b]));
+  const int m0 = mblk * kBM;
+  const int kend = causal ? min(kv_lim, m0 + kBM) : kv_lim;
+  const int ntiles = (kend + kBN - 1) / kBN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int qi = lane & 31, hh = lane >> 5;
+  const int g = lane >> 4, gi = lane & 15;
+  const int wq0 = m0 + wave * 32;
+  const int qrow = wq0 + qi;
+  const int qrow_c = min(qrow, N - 1);
+
+  u32x4 ks[kSC], vs[kSC];
+  auto load_tile = [&](int t) {
+    const int n0 = t * kBN;
+#pragma unroll
+    for (int j = 0; j < kSC; ++j) {
+      const int ci = tid + kThreads * j;
+      const int row = ci / kCPR, ch = ci % kCPR;
+      const size_t goff = head + (size_t)min(n0 + row, N - 1) * D + ch * 8;
+      ks[j] = *reinterpret_cast<const u32x4*>(K + goff);
+      vs[j] = *reinterpret_cast<const u32x4*>(V + goff);
+    }
+  };
+  auto store_tile = [&](FA_LDS uint8_t* kb, FA_LDS uint8_t* vb) {
+#pragma unroll
+    for (int j = 0; j < kSC; ++j) {
+      const int ci = tid + kThreads * j;
+      const int row = ci / kCPR, ch = ci % kCPR;
+      lds_write16(kb + tile_off<D>(row, ch), to_f16x8<T>(ks[j]));
+      lds_write16(vb + tile_off<D>(row, ch), to_f16x8<T>(vs[j]));
+    }
+  };
+
+  if (ntiles > 0) load_tile(0);
+
+  // this lane's query row of Q and dO as B operands (fp16): [query][16c + 8hh + 0..7]
+  u32x4 qf[kKC], of[kKC];
+#pragma unroll
+  for (int c = 0; c < kKC; ++c) {
+    const size_t off = head + (size_t)qrow_c * D + 16 * c + 8 * hh;
+    qf[c] = to_f16x8<T>(*reinterpret_cast<const u32x4*>(Q + off));
+    of[c] = to_f16x8<T>(*reinterpret_cast<const u32x4*>(dO + off));
+  }
+  const float lse2 = LSE[(size_t)bh * N + qrow_c] * kLog2e;
+  const float dlt = delta[(size_t)bh * N + qrow_c];
+  f32x16 dqacc[kDB];
+#pragma unroll
+  for (int i = 0; i < kDB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqacc[i][r] = 0.f;
+  const int krow_base = kappa(qi);
+
+  if (ntiles > 0) store_tile((FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Vb0);
+
+  auto step = [&](int t, const FA_LDS uint8_t* Ks, const FA_LDS uint8_t* Vs, FA_LDS uint8_t* Kn,
+                  FA_LDS uint8_t* Vn) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile(t + 1);
+    const int n0 = t * kBN;
+    const bool need_mask = (n0 + kBN > kv_lim) || (causal && n0 + kBN - 1 > wq0);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const bool vis = (n0 + 32 * sub < kv_lim) && (!causal || n0 + 32 * sub <= wq0 + 31);
+      if (!vis) continue;
+      // S^T = K Q^T and dP^T = V dO^T for 32 keys; lane (query, hh), register r <->
+      // key n0 + 32*sub + 16*(r/8) + 8*hh + r%8
+      f32x16 st, dpt;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        st[r] = 0.f;
+        dpt[r] = 0.f;
+      }
+      const int krow = sub * 32 + krow_base;
+#pragma unroll
+      for (int c = 0; c < kKC; ++c) {
+        const int off = tile_off<D>(krow, 2 * c + hh);
+        st = Mfma<F16>::run(lds_read16(Ks + off), qf[c], st);
+        dpt = Mfma<F16>::run(lds_read16(Vs + off), of[c], dpt);
+      }
+      uint32_t dsk[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float ds2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * i + e;
+          float p = exp2_fast(fmaf(st[r], sl2, -lse2));
+          if (need_mask) {
+            const int kk = n0 + 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
+            const bool hide = kk >= kv_lim || (causal && kk > qrow);
+            p = hide ? 0.f : p;
+          }
+          ds2[e] = p * (dpt[r] - dlt);
+        }
+        dsk[i] = Mfma<F16>::pack(ds2[0], ds2[1]);
+      }
+      // dQ^T += K^T dS^T: two 16-key steps; K^T through the transposing read
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const u32x4 bs = {dsk[4 * c2], dsk[4 * c2 + 1], dsk[4 * c2 + 2], dsk[4 * c2 + 3]};
+        const int trow = 32 * sub + 16 * c2 + 8 * hh + (gi >> 2);
+        const int inner = 8 * (gi & 1);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const int ch = db * 4 + 2 * (g & 1) + ((gi & 3) >> 1);
+          const u32x2 lo = lds_read_tr16(Ks + tile_off<D>(trow, ch) + inner);
+          const u32x2 hi = lds_read_tr16(Ks + tile_off<D>(trow + 4, ch) + inner);
+          dqacc[db] = Mfma<F16>::run(u32x4{lo[0], lo[1], hi[0], hi[1]}, bs, dqacc[db]);
+        }
+      }
+    }
+    if (more) store_tile(Kn, Vn);
+  };
+
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, (const FA_LDS uint8_t*)Kb0, (const FA_LDS uint8_t*)Vb0, (FA_LDS uint8_t*)Kb1,
+         (FA_LDS uint8_t*)Vb1);
+    if (t + 1 < ntiles)
+      step(t + 1, (const FA_LDS uint8_t*)Kb1, (const FA_LDS uint8_t*)Vb1, (FA_LDS uint8_t*)Kb0,
+           (FA_LDS uint8_t*)Vb0);
+  }
+
+  // dQ = scale * dQ_acc: lane (query, hh), register r <-> d = 32db + 8(r/4) + 4hh + r%4
+  if (qrow < N) {
+    float* dqr = dQ + head + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 val = {scale * dqacc[db][4 * a4 + 0], scale * dqacc[db][4 * a4 + 1],
+                           scale * dqacc[db][4 * a4 + 2], scale * dqacc[db][4 * a4 + 3]};
+        *reinterpret_cast<f32x4*>(dqr + db * 32 + 8 * a4 + 4 * hh) = val;
+      }
+  }
+}
+
 }  // namespace
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d) {
@@ -361,41 +475,35 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d) {
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+  if (a.dtype == kDtypeF32) return hipErrorNotSupported;  // rejected by the API layer
   const int BH = a.B * a.H;
   const size_t rows = (size_t)BH * a.N;
-  const size_t pre_threads = rows * (a.d / 8);
-  const int pre_blocks = (int)((pre_threads + kThreads - 1) / kThreads);
+  const int pre_blocks = (int)((rows * (a.d / 8) + kThreads - 1) / kThreads);
   const float sl2 = a.scale * kLog2e;
-  if (a.dtype == kDtypeF32) return hipErrorNotSupported;  // rejected by the API layer
-  const auto* dO16 = static_cast<const uint16_t*>(a.dout);
-#define FA_PRE(TAG, DIM)                                                                  \
-  hipLaunchKernelGGL((bwd_pre_kernel<TAG, DIM>), dim3(pre_blocks), dim3(kThreads), 0, stream, \
-                     dO16, a.o, a.delta, a.dq, rows)
-  if (a.dtype == kDtypeBF16) {
-    if (a.d == 64) FA_PRE(BF16, 64); else FA_PRE(BF16, 128);
-  } else {
-    if (a.d == 64) FA_PRE(F16, 64); else FA_PRE(F16, 128);
-  }
-#undef FA_PRE
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  const int n_kblk = (a.N + kBK - 1) / kBK;
   const int hpx = (BH + 7) / 8;
-  const int blocks = 8 * hpx * n_kblk;
+  const int n_kblk = (a.N + kBK - 1) / kBK;
+  const int n_mblk = (a.N + kBM - 1) / kBM;
   const auto* q16 = static_cast<const uint16_t*>(a.q);
   const auto* k16 = static_cast<const uint16_t*>(a.k);
   const auto* v16 = static_cast<const uint16_t*>(a.v);
-#define FA_MAIN(TAG, DIM)                                                                   \
-  hipLaunchKernelGGL((bwd_main_kernel<TAG, DIM>), dim3(blocks), dim3(kThreads), 0, stream, \
-                     q16, k16, v16, dO16, a.lse, a.delta, a.dq, a.dk, a.dv, BH, a.H, a.N,   \
-                     a.scale, sl2, a.causal, a.kv_len, n_kblk, hpx)
+  const auto* dO16 = static_cast<const uint16_t*>(a.dout);
+#define FA_BWD_LAUNCH(TAG, DIM)                                                              \
+  do {                                                                                       \
+    hipLaunchKernelGGL((bwd_pre_kernel<TAG, DIM>), dim3(pre_blocks), dim3(kThreads), 0,      \
+                       stream, dO16, a.o, a.delta, rows);                                    \
+    hipLaunchKernelGGL((bwd_dkdv_kernel<TAG, DIM>), dim3(8 * hpx * n_kblk), dim3(kThreads),  \
+                       0, stream, q16, k16, v16, dO16, a.lse, a.delta, a.dk, a.dv, BH, a.H,  \
+                       a.N, a.scale, sl2, a.causal, a.kv_len, n_kblk, hpx);                  \
+    hipLaunchKernelGGL((bwd_dq_kernel<TAG, DIM>), dim3(8 * hpx * n_mblk), dim3(kThreads), 0, \
+                       stream, q16, k16, v16, dO16, a.lse, a.delta, a.dq, BH, a.H, a.N,      \
+                       a.scale, sl2, a.causal, a.kv_len, n_mblk, hpx);                       \
+  } while (0)
   if (a.dtype == kDtypeBF16) {
-    if (a.d == 64) FA_MAIN(BF16, 64); else FA_MAIN(BF16, 128);
+    if (a.d == 64) FA_BWD_LAUNCH(BF16, 64); else FA_BWD_LAUNCH(BF16, 128);
   } else {
-    if (a.d == 64) FA_MAIN(F16, 64); else FA_MAIN(F16, 128);
+    if (a.d == 64) FA_BWD_LAUNCH(F16, 64); else FA_BWD_LAUNCH(F16, 128);
   }
-#undef FA_MAIN
+#undef FA_BWD_LAUNCH
   return hipGetLastError();
 }
 

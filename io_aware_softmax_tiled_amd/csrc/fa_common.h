@@ -73,6 +73,31 @@ __device__ inline uint32_t bf16x2_to_f16x2(uint32_t x) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// 8 input elements (16 bytes of bf16 or f16) -> 8 fp16
+template <typename T> __device__ inline u32x4 to_f16x8(u32x4 x);
+template <> __device__ inline u32x4 to_f16x8<F16>(u32x4 x) { return x; }
+template <> __device__ inline u32x4 to_f16x8<BF16>(u32x4 x) {
+  return {bf16x2_to_f16x2(x[0]), bf16x2_to_f16x2(x[1]), bf16x2_to_f16x2(x[2]),
+          bf16x2_to_f16x2(x[3])};
+}
+
+// swap bits 2 and 3 of a row index in [0, 32): reading A-operand rows in this order
+// makes accumulator register r of lane l hold row 16*(r/8) + 8*(l/32) + r%8, i.e. each
+// lane's 8 consecutive registers cover 8 consecutive rows
+__device__ inline int kappa(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// blockIdx.x -> (head, block): XCD-major (blocks of one head on one XCD), block index
+// `slot / heads_per_xcd` from 0
+struct WgPos {
+  int bh, blk;
+};
+__device__ inline WgPos wg_position(int heads_per_xcd) {
+  const int w = blockIdx.x;
+  const int xcd = w & 7;
+  const int slot = w >> 3;
+  return {(slot % heads_per_xcd) * 8 + xcd, slot / heads_per_xcd};
+}
+
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 

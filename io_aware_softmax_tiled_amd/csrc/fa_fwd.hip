@@ -43,36 +43,9 @@ constexpr int kBM = 128;   // query rows per workgroup (4 waves x 32)
 constexpr int kBN = 64;    // key rows per tile
 constexpr int kThreads = 256;
 
-// swap bits 2 and 3 of a row index in [0, 32)
-__device__ inline int kappa(int m) {
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
-
-struct WgPos {
-  int bh, mblk;
-};
-
-// blockIdx.x -> (head, query block): XCD-major, heaviest query block first.
-__device__ inline WgPos wg_position(int BH, int n_mblk, int heads_per_xcd) {
-  const int w = blockIdx.x;
-  const int xcd = w & 7;
-  const int slot = w >> 3;
-  const int hx = slot % heads_per_xcd;
-  const int mrev = slot / heads_per_xcd;
-  return {hx * 8 + xcd, n_mblk - 1 - mrev};
-}
-
 // ---------------------------------------------------------------------------------
 // 16-bit inputs (bf16 or f16)
 // ---------------------------------------------------------------------------------
-// 8 input elements (16 bytes of bf16 or f16) -> 8 fp16
-template <typename T> __device__ inline u32x4 to_f16x8(u32x4 x);
-template <> __device__ inline u32x4 to_f16x8<F16>(u32x4 x) { return x; }
-template <> __device__ inline u32x4 to_f16x8<BF16>(u32x4 x) {
-  return {bf16x2_to_f16x2(x[0]), bf16x2_to_f16x2(x[1]), bf16x2_to_f16x2(x[2]),
-          bf16x2_to_f16x2(x[3])};
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel_16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -92,8 +65,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel_16(
   __shared__ __attribute__((aligned(1024))) uint8_t Vb0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t Vb1[kTileBytes];
 
-  const WgPos pos = wg_position(BH, n_mblk, heads_per_xcd);
+  const WgPos pos = wg_position(heads_per_xcd);
   if (pos.bh >= BH) return;
+  const int mblk = n_mblk - 1 - pos.blk;  // heaviest query block first
   const int b = pos.bh / H;
   const size_t head = (size_t)pos.bh * N * D;
   const uint16_t* q = Q + head;
@@ -102,7 +76,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel_16(
 
   int kv_lim = N;
   if (kv_len != nullptr) kv_lim = min(N, max(1, kv_len[b]));
-  const int m0 = pos.mblk * kBM;
+  const int m0 = mblk * kBM;
   const int kend = causal ? min(kv_lim, m0 + kBM) : kv_lim;
   const int ntiles = (kend + kBN - 1) / kBN;
 
@@ -315,8 +289,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel_f32(
   __shared__ __attribute__((aligned(16))) float Ks[kBN * kLd];
   __shared__ __attribute__((aligned(16))) float Vs[kBN * kLd];
 
-  const WgPos pos = wg_position(BH, n_mblk, heads_per_xcd);
+  const WgPos pos = wg_position(heads_per_xcd);
   if (pos.bh >= BH) return;
+  const int mblk = n_mblk - 1 - pos.blk;  // heaviest query block first
   const int b = pos.bh / H;
   const size_t head = (size_t)pos.bh * N * D;
   const float* q = Q + head;
@@ -324,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel_f32(
   const float* v = V + head;
   int kv_lim = N;
   if (kv_len != nullptr) kv_lim = min(N, max(1, kv_len[b]));
-  const int m0 = pos.mblk * kBM;
+  const int m0 = mblk * kBM;
   const int kend = causal ? min(kv_lim, m0 + kBM) : kv_lim;
   const int ntiles = (kend + kBN - 1) / kBN;
 

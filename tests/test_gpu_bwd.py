@@ -86,11 +86,11 @@ def test_bwd_gradient_sums():
     assert (dv.double().sum(2).cpu() - do.sum(2)).abs().max() < 5e-2
 
 
-def test_bwd_repeatable():
-    """dK and dV are bit-identical across runs; dQ (fp32 atomics) agrees to rounding."""
+def test_bwd_deterministic():
+    """Every gradient is written once (no atomics): runs are bit-identical."""
     w, inp = workloads.custom(2, 2, 640, 64, "bf16", True, kv_range=(300, 640), seed=24)
     dev = U.to_dev(inp)
     r1 = U.gpu_bwd(inp, dev)
     r2 = U.gpu_bwd(inp, dev)
-    assert torch.equal(r1[3], r2[3]) and torch.equal(r1[4], r2[4])
-    assert (r1[2] - r2[2]).abs().max().item() < 1e-5
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
