@@ -126,6 +126,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="also print one line per sequence length (supplementary)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first copy a MIB-MiB buffer once (a plain copy kernel of known size, "
+                         "to calibrate HBM byte counters in a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -141,6 +144,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     fa.load_library()
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = workloads.WORKLOADS[WORKLOAD_ID]
     inp = workloads.draw(w)
     ms_step, fwd_ms, bwd_ms = bench_workload(fa, torch, w, inp, args.steps, args.warmup)
