@@ -11,7 +11,7 @@
 // Kernels (no atomics; every output is written once, so all of them are deterministic):
 // 1. bwd_pre: D_i = rowsum(dO * O) into the workspace.
 // 2. bwd_dkdv: one workgroup per 128 keys of one (batch, head), 32 keys per wave, keys
-//    on lanes. It loops over 32-query tiles (causal: from the block's diagonal on),
+//    on lanes. It loops over 64-query tiles (causal: from the block's diagonal on),
 //    recomputes S = Q K^T and dP = dO V^T, forms P and dS in registers, and accumulates
 //    dV^T += dO^T P and dK^T += Q^T dS in registers (dO^T and Q^T through the
 //    transposing LDS read). Q/dO tiles are prefetched one tile ahead and
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
 // 2. dK, dV: keys on lanes
 // ---------------------------------------------------------------------------------
 constexpr int kBK = 128;  // keys per workgroup
-constexpr int kBQ = 32;   // queries per tile
+constexpr int kBQ = 64;   // queries per tile (two 32-query halves)
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
@@ -187,10 +187,91 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       dvacc[i][r] = 0.f;
     }
   const bool wave_dead = kw0 >= kv_lim;
-  const int arow = kappa(li);  // A-operand row (query) read by this lane
+
+  // Per-lane byte offsets inside a Q or dO tile, fixed for the whole loop (the
+  // swizzle depends on the low 4 bits of the row only, so 16- and 32-row steps and
+  // the buffer choice are immediate offsets).
+  int aoff[kKC];  // A-operand rows (queries, order kappa) for S = Q K^T and dP = dO V^T
+#pragma unroll
+  for (int c = 0; c < kKC; ++c) aoff[c] = tile_off<D>(kappa(li), 2 * c + hh);
+  int toff[2][kDB];  // transposing reads of dO^T and Q^T
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+      toff[r][db] = tile_off<D>(8 * hh + (gi >> 2) + 4 * r, db * 4 + 2 * (g & 1) + ((gi & 3) >> 1)) +
+                    8 * (gi & 1);
 
   if (i0 < nq) store_tile((FA_LDS uint8_t*)Qb0, (FA_LDS uint8_t*)Ob0, (FA_LDS float*)St0);
 
+  // S = Q K^T and dP = dO V^T for the 32 queries of half `hf`:
+  // lane (key, hh), register r <-> query q0 + 32*hf + 16*(r/8) + 8*hh + r%8
+  auto products = [&](const FA_LDS uint8_t* Qc, const FA_LDS uint8_t* Oc, int hf, f32x16& s,
+                      f32x16& dp) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      dp[r] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < kKC; ++c) {
+      const int off = aoff[c] + hf * 32 * D * 2;
+      s = Mfma<F16>::run(lds_read16(Qc + off), kf[c], s);
+      dp = Mfma<F16>::run(lds_read16(Oc + off), vf[c], dp);
+    }
+  };
+  // P and dS for half `hf`, then dV^T += dO^T P and dK^T += Q^T dS
+  auto accumulate = [&](const FA_LDS uint8_t* Qc, const FA_LDS uint8_t* Oc, const FA_LDS float* Stc,
+                        int q0, int hf, const f32x16& s, const f32x16& dp, bool need_mask) {
+    uint32_t pp[8], dsp[8];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int qb = 32 * hf + 16 * c + 8 * hh;
+      const f32x4 l0 = *reinterpret_cast<const FA_LDS f32x4*>(&Stc[qb]);
+      const f32x4 l1 = *reinterpret_cast<const FA_LDS f32x4*>(&Stc[qb + 4]);
+      const f32x4 d0 = *reinterpret_cast<const FA_LDS f32x4*>(&Stc[kBQ + qb]);
+      const f32x4 d1 = *reinterpret_cast<const FA_LDS f32x4*>(&Stc[kBQ + qb + 4]);
+      float p[8], ds[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 8 * c + j;
+        const float lq = j < 4 ? l0[j] : l1[j - 4];
+        const float dq = j < 4 ? d0[j] : d1[j - 4];
+        float pj = exp2_fast(fmaf(s[r], sl2, -lq));
+        if (need_mask) {
+          const int qq = q0 + qb + j;
+          const bool hide = qq >= N || key >= kv_lim || (causal && key > qq);
+          pj = hide ? 0.f : pj;
+        }
+        p[j] = pj;
+        ds[j] = pj * (dp[r] - dq);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pp[4 * c + j] = Mfma<F16>::pack(p[2 * j], p[2 * j + 1]);
+        dsp[4 * c + j] = Mfma<F16>::pack(ds[2 * j], ds[2 * j + 1]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const u32x4 bp = {pp[4 * c], pp[4 * c + 1], pp[4 * c + 2], pp[4 * c + 3]};
+      const u32x4 bs = {dsp[4 * c], dsp[4 * c + 1], dsp[4 * c + 2], dsp[4 * c + 3]};
+      const int rows = (32 * hf + 16 * c) * D * 2;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const u32x2 a0 = lds_read_tr16(Oc + toff[0][db] + rows);
+        const u32x2 a1 = lds_read_tr16(Oc + toff[1][db] + rows);
+        dvacc[db] = Mfma<F16>::run(u32x4{a0[0], a0[1], a1[0], a1[1]}, bp, dvacc[db]);
+        const u32x2 b0 = lds_read_tr16(Qc + toff[0][db] + rows);
+        const u32x2 b1 = lds_read_tr16(Qc + toff[1][db] + rows);
+        dkacc[db] = Mfma<F16>::run(u32x4{b0[0], b0[1], b1[0], b1[1]}, bs, dkacc[db]);
+      }
+    }
+  };
+
+  // one 64-query tile: publish it (barrier), prefetch the next one, issue the S and dP
+  // products of both halves, then finish half 0 (vector work overlapping half 1's
+  // products) and half 1.
   auto step = [&](int it, const FA_LDS uint8_t* Qc, const FA_LDS uint8_t* Oc,
                   const FA_LDS float* Stc, FA_LDS uint8_t* Qn, FA_LDS uint8_t* On,
                   FA_LDS float* Stn) {
@@ -199,70 +280,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bool more = it + 1 < nq;
     if (more) load_tile(it + 1);
     const int q0 = it * kBQ;
+    // a tile entirely above this wave's keys' diagonal (or a wave whose keys are all
+    // padded) is skipped; otherwise both halves run, and a half hidden from every key is
+    // masked to P = 0 like any other hidden entry (one code path: no accumulator copies)
     const bool active = !wave_dead && !(causal && kw0 > q0 + kBQ - 1);
+    const bool need_mask =
+        (causal && kw0 + 31 > q0) || (q0 + kBQ > N) || (kw0 + 32 > kv_lim);
     if (active) {
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
-#pragma unroll
-      for (int c = 0; c < kKC; ++c) {
-        const int off = tile_off<D>(arow, 2 * c + hh);
-        s = Mfma<F16>::run(lds_read16(Qc + off), kf[c], s);
-        dp = Mfma<F16>::run(lds_read16(Oc + off), vf[c], dp);
-      }
-      // lane (key, hh), register r <-> query q0 + 16*(r/8) + 8*hh + r%8
-      const bool need_mask =
-          (causal && kw0 + 31 > q0) || (q0 + kBQ > N) || (kw0 + 32 > kv_lim);
-      uint32_t pp[8], dsp[8];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int qb = 16 * c + 8 * hh;
-        const f32x4 l0 = *reinterpret_cast<const FA_LDS f32x4*>(&Stc[qb]);
-        const f32x4 l1 = *reinterpret_cast<const FA_LDS f32x4*>(&Stc[qb + 4]);
-        const f32x4 d0 = *reinterpret_cast<const FA_LDS f32x4*>(&Stc[kBQ + qb]);
-        const f32x4 d1 = *reinterpret_cast<const FA_LDS f32x4*>(&Stc[kBQ + qb + 4]);
-        float p[8], ds[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 8 * c + j;
-          const float lq = j < 4 ? l0[j] : l1[j - 4];
-          const float dq = j < 4 ? d0[j] : d1[j - 4];
-          float pj = exp2_fast(fmaf(s[r], sl2, -lq));
-          if (need_mask) {
-            const int qq = q0 + qb + j;
-            const bool hide = qq >= N || key >= kv_lim || (causal && key > qq);
-            pj = hide ? 0.f : pj;
-          }
-          p[j] = pj;
-          ds[j] = pj * (dp[r] - dq);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          pp[4 * c + j] = Mfma<F16>::pack(p[2 * j], p[2 * j + 1]);
-          dsp[4 * c + j] = Mfma<F16>::pack(ds[2 * j], ds[2 * j + 1]);
-        }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS; A operands through the transposing read
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const u32x4 bp = {pp[4 * c], pp[4 * c + 1], pp[4 * c + 2], pp[4 * c + 3]};
-        const u32x4 bs = {dsp[4 * c], dsp[4 * c + 1], dsp[4 * c + 2], dsp[4 * c + 3]};
-        const int trow = 16 * c + 8 * hh + (gi >> 2);
-        const int inner = 8 * (gi & 1);
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          const int ch = db * 4 + 2 * (g & 1) + ((gi & 3) >> 1);
-          const u32x2 a0 = lds_read_tr16(Oc + tile_off<D>(trow, ch) + inner);
-          const u32x2 a1 = lds_read_tr16(Oc + tile_off<D>(trow + 4, ch) + inner);
-          dvacc[db] = Mfma<F16>::run(u32x4{a0[0], a0[1], a1[0], a1[1]}, bp, dvacc[db]);
-          const u32x2 b0 = lds_read_tr16(Qc + tile_off<D>(trow, ch) + inner);
-          const u32x2 b1 = lds_read_tr16(Qc + tile_off<D>(trow + 4, ch) + inner);
-          dkacc[db] = Mfma<F16>::run(u32x4{b0[0], b0[1], b1[0], b1[1]}, bs, dkacc[db]);
-        }
-      }
+      f32x16 s0, dp0, s1, dp1;
+      products(Qc, Oc, 0, s0, dp0);
+      products(Qc, Oc, 1, s1, dp1);
+      accumulate(Qc, Oc, Stc, q0, 0, s0, dp0, need_mask);
+      accumulate(Qc, Oc, Stc, q0, 1, s1, dp1, need_mask);
     }
     if (more) store_tile(Qn, On, Stn);
   };

@@ -145,10 +145,90 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel_16(
   const int krow_base = kappa(qi);
   const int g = lane >> 4, gi = lane & 15;
 
+  // Per-lane byte offsets inside a K or V tile, fixed for the whole loop. The swizzle
+  // depends only on the low 4 bits of the row, so moving by 16 or 32 rows (and between
+  // the two buffers) is a compile-time constant the LDS instructions take as an
+  // immediate offset.
+  int koff[kKC];
+#pragma unroll
+  for (int c = 0; c < kKC; ++c) koff[c] = tile_off<D>(krow_base, 2 * c + hh);
+  int voff[2][kDB];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+      voff[r][db] = tile_off<D>(8 * hh + (gi >> 2) + 4 * r, db * 4 + 2 * (g & 1) + ((gi & 3) >> 1)) +
+                    8 * (gi & 1);
+
   if (ntiles > 0) store_v((FA_LDS uint8_t*)Vb0);
 
+  // S^T for the 32 keys of block `sub` of the tile in Ks
+  auto scores = [&](const FA_LDS uint8_t* Ks, int sub) {
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < kKC; ++c)
+      acc = Mfma<T>::run(lds_read16(Ks + koff[c] + sub * 32 * D * 2), qf[c], acc);
+    return acc;
+  };
+  // one online-softmax step over 32 keys (the tiled recurrence with tile width 32),
+  // then O^T += V^T P^T for those keys
+  auto softmax_pv = [&](f32x16 s, const FA_LDS uint8_t* Vs, int sub) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[r], s[r + 1]);
+    mx = max_halves(mx);  // both halves of the wave hold the same query rows
+    // a row raises its reference maximum only when the exponent would exceed 2^8; the
+    // decision is per row, so each row's arithmetic depends on its own scores only
+    const bool grow = (mx - m_ref) * sl2 > 8.0f;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_ref;
+      const float alpha = exp2_fast((m_ref - m_new) * sl2);  // 1 if kept, 0 from -inf
+      m_ref = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < kDB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+    }
+    // P = exp2(s*scale*log2e - m_ref*scale*log2e), rounded to fp16, and its row sum
+    const float nms = -m_ref * sl2;
+    uint32_t pk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p0 = exp2_fast(fmaf(s[2 * i], sl2, nms));
+      const float p1 = exp2_fast(fmaf(s[2 * i + 1], sl2, nms));
+      pk[i] = Mfma<F16>::pack(p0, p1);
+      lsum = Mfma<F16>::dot_ones(pk[i], lsum);
+    }
+    // two 16-key steps; V^T through the transposing read
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const u32x4 bp = {pk[4 * c2], pk[4 * c2 + 1], pk[4 * c2 + 2], pk[4 * c2 + 3]};
+      const int rows = (32 * sub + 16 * c2) * D * 2;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const u32x2 lo = lds_read_tr16(Vs + voff[0][db] + rows);
+        const u32x2 hi = lds_read_tr16(Vs + voff[1][db] + rows);
+        oacc[db] = Mfma<F16>::run(u32x4{lo[0], lo[1], hi[0], hi[1]}, bp, oacc[db]);
+      }
+    }
+  };
+  // -inf where key j is hidden from this lane's query (diagonal, padding or sequence end)
+  auto mask = [&](f32x16& s, int n0, int sub) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = n0 + 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
+      const bool hide = key >= kv_lim || (causal && key > qrow);
+      s[r] = hide ? -INFINITY : s[r];
+    }
+  };
+
   // one tile: publish it (barrier), start fetching the next one into the other buffer,
-  // then run the online-softmax update on this one
+  // then run two 32-key online-softmax steps on it. Both blocks' score products are
+  // issued before the first softmax, so the matrix cores work on block 1 while the
+  // vector units exponentiate block 0, and on P V of block 0 while they do block 1.
   auto step = [&](int t, const FA_LDS uint8_t* Ks, const FA_LDS uint8_t* Vs,
                   FA_LDS uint8_t* Kn, FA_LDS uint8_t* Vn) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -159,94 +239,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel_16(
       load_v(t + 1);
     }
     const int n0 = t * kBN;
-    bool vis[2];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-      vis[sub] = (n0 + 32 * sub < kv_lim) && (!causal || n0 + 32 * sub <= wq0 + 31);
-    if (vis[0] || vis[1]) {
-      f32x16 sacc[2];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[sub][r] = 0.f;
-        if (vis[sub]) {
-          const int krow = sub * 32 + krow_base;
-#pragma unroll
-          for (int c = 0; c < kKC; ++c) {
-            const u32x4 a = lds_read16(Ks + tile_off<D>(krow, 2 * c + hh));
-            sacc[sub] = Mfma<T>::run(a, qf[c], sacc[sub]);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[sub][r] = -INFINITY;
-        }
-      }
-
-      // masks: only on tiles crossing the diagonal, the padding bound or the end
-      const bool need_mask = (n0 + kBN > kv_lim) || (causal && n0 + kBN - 1 > wq0);
+    // a tile with no key visible to this wave is skipped; otherwise both 32-key blocks
+    // run, and a block hidden from the whole wave is masked to -inf like any other
+    // hidden key (so the code has one path and the accumulators are never copied)
+    const bool vis = (n0 < kv_lim) && (!causal || n0 <= wq0 + 31);
+    const bool need_mask = (n0 + kBN > kv_lim) || (causal && n0 + kBN - 1 > wq0);
+    if (vis) {
+      f32x16 s0 = scores(Ks, 0);
+      f32x16 s1 = scores(Ks, 1);
       if (need_mask) {
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = n0 + 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
-            const bool hide = key >= kv_lim || (causal && key > qrow);
-            sacc[sub][r] = hide ? -INFINITY : sacc[sub][r];
-          }
+        mask(s0, n0, 0);
+        mask(s1, n0, 1);
       }
-
-      // row maximum of this tile (both halves of the wave hold the same query rows)
-      float mx = -INFINITY;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = max3f(mx, sacc[sub][r], sacc[sub][r + 1]);
-      mx = max_halves(mx);
-
-      // a row raises its reference maximum only when the exponent would exceed 2^8;
-      // the decision is per row, so each row's arithmetic depends on its own scores only
-      const bool grow = (mx - m_ref) * sl2 > 8.0f;
-      if (__any(grow)) {
-        const float m_new = grow ? mx : m_ref;
-        const float alpha = exp2_fast((m_ref - m_new) * sl2);  // 1 if kept, 0 from -inf
-        m_ref = m_new;
-        lsum *= alpha;
-#pragma unroll
-        for (int i = 0; i < kDB; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-      }
-
-      // P = exp2(s*scale*log2e - m_ref*scale*log2e), rounded to fp16, and its row sum
-      const float nms = -m_ref * sl2;
-      uint32_t pk[2][8];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float p0 = exp2_fast(fmaf(sacc[sub][2 * i], sl2, nms));
-          const float p1 = exp2_fast(fmaf(sacc[sub][2 * i + 1], sl2, nms));
-          pk[sub][i] = Mfma<F16>::pack(p0, p1);
-          lsum = Mfma<F16>::dot_ones(pk[sub][i], lsum);
-        }
-
-      // O^T += V^T P^T: four 16-key steps per tile
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (!vis[c >> 1]) continue;
-        const u32x4 bp = {pk[c >> 1][4 * (c & 1) + 0], pk[c >> 1][4 * (c & 1) + 1],
-                          pk[c >> 1][4 * (c & 1) + 2], pk[c >> 1][4 * (c & 1) + 3]};
-        const int vrow = 16 * c + 8 * hh + (gi >> 2);
-        const int inner = 8 * (gi & 1);
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          const int vch = db * 4 + 2 * (g & 1) + ((gi & 3) >> 1);
-          const u32x2 lo = lds_read_tr16(Vs + tile_off<D>(vrow, vch) + inner);
-          const u32x2 hi = lds_read_tr16(Vs + tile_off<D>(vrow + 4, vch) + inner);
-          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[db] = Mfma<F16>::run(a, bp, oacc[db]);
-        }
-      }
+      softmax_pv(s0, Vs, 0);
+      softmax_pv(s1, Vs, 1);
     }
     if (more) store_v(Vn);
   };
