@@ -220,9 +220,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       dp = Mfma<F16>::run(lds_read16(Oc + off), vf[c], dp);
     }
   };
-  // P and dS for half `hf`, then dV^T += dO^T P and dK^T += Q^T dS
+  // -inf where the query does not see this lane's key (diagonal, padding, sequence end)
+  auto mask = [&](f32x16& s, int q0, int hf) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qq = q0 + 32 * hf + 16 * (r >> 3) + 8 * hh + (r & 7);
+      const bool hide = qq >= N || key >= kv_lim || (causal && key > qq);
+      s[r] = hide ? -INFINITY : s[r];
+    }
+  };
+  // P and dS for half `hf` (masked scores are -inf, so P = dS = 0 there), then
+  // dV^T += dO^T P and dK^T += Q^T dS
   auto accumulate = [&](const FA_LDS uint8_t* Qc, const FA_LDS uint8_t* Oc, const FA_LDS float* Stc,
-                        int q0, int hf, const f32x16& s, const f32x16& dp, bool need_mask) {
+                        int hf, const f32x16& s, const f32x16& dp) {
     uint32_t pp[8], dsp[8];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -237,12 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         const int r = 8 * c + j;
         const float lq = j < 4 ? l0[j] : l1[j - 4];
         const float dq = j < 4 ? d0[j] : d1[j - 4];
-        float pj = exp2_fast(fmaf(s[r], sl2, -lq));
-        if (need_mask) {
-          const int qq = q0 + qb + j;
-          const bool hide = qq >= N || key >= kv_lim || (causal && key > qq);
-          pj = hide ? 0.f : pj;
-        }
+        const float pj = exp2_fast(fmaf(s[r], sl2, -lq));
         p[j] = pj;
         ds[j] = pj * (dp[r] - dq);
       }
@@ -290,8 +295,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       f32x16 s0, dp0, s1, dp1;
       products(Qc, Oc, 0, s0, dp0);
       products(Qc, Oc, 1, s1, dp1);
-      accumulate(Qc, Oc, Stc, q0, 0, s0, dp0, need_mask);
-      accumulate(Qc, Oc, Stc, q0, 1, s1, dp1, need_mask);
+      if (need_mask) {
+        mask(s0, q0, 0);
+        mask(s1, q0, 1);
+      }
+      accumulate(Qc, Oc, Stc, 0, s0, dp0);
+      accumulate(Qc, Oc, Stc, 1, s1, dp1);
     }
     if (more) store_tile(Qn, On, Stn);
   };
@@ -438,22 +447,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         st = Mfma<F16>::run(lds_read16(Ks + off), qf[c], st);
         dpt = Mfma<F16>::run(lds_read16(Vs + off), of[c], dpt);
       }
+      if (need_mask) {  // -inf where the key is hidden from this lane's query
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = n0 + 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
+          const bool hide = kk >= kv_lim || (causal && kk > qrow);
+          st[r] = hide ? -INFINITY : st[r];
+        }
+      }
       uint32_t dsk[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float ds2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int r = 2 * i + e;
-          float p = exp2_fast(fmaf(st[r], sl2, -lse2));
-          if (need_mask) {
-            const int kk = n0 + 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
-            const bool hide = kk >= kv_lim || (causal && kk > qrow);
-            p = hide ? 0.f : p;
-          }
-          ds2[e] = p * (dpt[r] - dlt);
-        }
-        dsk[i] = Mfma<F16>::pack(ds2[0], ds2[1]);
+        const float p0 = exp2_fast(fmaf(st[2 * i], sl2, -lse2));
+        const float p1 = exp2_fast(fmaf(st[2 * i + 1], sl2, -lse2));
+        dsk[i] = Mfma<F16>::pack(p0 * (dpt[2 * i] - dlt), p1 * (dpt[2 * i + 1] - dlt));
       }
       // dQ^T += K^T dS^T: two 16-key steps; K^T through the transposing read
 #pragma unroll
