@@ -129,6 +129,12 @@ __device__ inline u32x2 lds_read_tr16(const FA_LDS uint8_t* p) {
   return __builtin_bit_cast(u32x2, t);
 }
 
+// Workgroup barrier that hands LDS data between waves: it waits for this wave's LDS
+// operations only, not for its outstanding global loads, so prefetches issued before it
+// stay in flight across it (__syncthreads() also waits for every global load). The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ inline void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
 // lds_base + 16*l (lds_base wave-uniform).
 __device__ inline void global_to_lds16(const void* gptr, FA_LDS void* lds_base) {

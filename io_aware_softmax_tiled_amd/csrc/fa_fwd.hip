@@ -20,8 +20,11 @@
 //   packed P feeds the P V product as its B operand with no data movement.
 // * O^T = V^T P^T takes V^T through the transposing LDS read, so V is staged in LDS
 //   row-major exactly like K.
-// * K and V tiles go global -> LDS with the direct LDS load (no VGPR staging),
-//   double-buffered, into an XOR-swizzled layout; one barrier per tile.
+// * K and V tiles are staged global -> registers -> LDS one tile ahead (V converted
+//   to fp16 on the way) into an XOR-swizzled layout, double-buffered; each step writes
+//   the next tile and starts the load of the one after before computing, so load and
+//   write latency hide under the compute; one barrier per tile, which waits for LDS
+//   traffic only.
 // * exp2 with scale*log2(e) folded into one FMA; the output is normalised once at the
 //   end (the pages normalise every step; the results are equal). The reference
 //   maximum used in the exponent is only raised when a tile's maximum exceeds it by
@@ -46,8 +49,11 @@ constexpr int kThreads = 256;
 // ---------------------------------------------------------------------------------
 // 16-bit inputs (bf16 or f16)
 // ---------------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel_16(
+// W waves per workgroup (4 or 8), 32 query rows each. With 8 waves every K/V tile
+// loaded into LDS serves 256 query rows, halving the tile traffic per FLOP; 4 waves
+// keep enough workgroups for small problems.
+template <typename T, int D, int W>
+__global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
     int BH, int H, int N, float scale, float sl2, int causal,
@@ -55,11 +61,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel_16(
   constexpr int kTileBytes = kBN * D * 2;              // one K or V tile
   constexpr int kKC = D / 16;                          // 16-wide k-steps over head_dim
   constexpr int kDB = D / 32;                          // 32-row blocks of O^T
-  constexpr int kKLoads = kTileBytes / 1024 / 4;       // direct K loads per wave per tile
   constexpr int kCPR = D / 8;                          // 16-byte chunks per row
-  constexpr int kVChunks = kTileBytes / 16 / kThreads; // V chunks per thread per tile
+  constexpr int kThr = W * 64;
+  constexpr int kBMw = W * 32;                         // query rows per workgroup
+  constexpr int kVChunks = kTileBytes / 16 / kThr;     // K/V chunks per thread per tile
   // two buffers, as separate arrays so the compiler can tell the tile being read from
-  // the tile being filled by the direct loads
+  // the tile being filled
   __shared__ __attribute__((aligned(1024))) uint8_t Kb0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t Kb1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t Vb0[kTileBytes];
@@ -76,8 +83,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel_16(
 
   int kv_lim = N;
   if (kv_len != nullptr) kv_lim = min(N, max(1, kv_len[b]));
-  const int m0 = mblk * kBM;
-  const int kend = causal ? min(kv_lim, m0 + kBM) : kv_lim;
+  const int m0 = mblk * kBMw;
+  const int kend = causal ? min(kv_lim, m0 + kBMw) : kv_lim;
   const int ntiles = (kend + kBN - 1) / kBN;
 
   const int tid = threadIdx.x;
@@ -89,44 +96,38 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel_16(
   const int qrow = wq0 + qi;
   const int qrow_c = min(qrow, N - 1);
 
-  // K tile t -> LDS by direct loads: each wave fills kKLoads 1 KB regions; lane l of a
-  // region fills its 16-byte slot l, so it fetches the chunk the swizzle puts there.
-  auto issue_k = [&](int t, FA_LDS uint8_t* kb) {
-    const int n0 = t * kBN;
-#pragma unroll
-    for (int j = 0; j < kKLoads; ++j) {
-      const int region = wave * kKLoads + j;
-      const int byte = region * 1024 + lane * 16;
-      const int row = byte / (D * 2);
-      const int pch = (byte % (D * 2)) >> 4;
-      const int lch = pch ^ chunk_swizzle<D>(row);
-      global_to_lds16(k + (size_t)min(n0 + row, N - 1) * D + lch * 8, kb + region * 1024);
-    }
-  };
-  // V tile t -> registers (coalesced 16-byte loads), later converted to fp16 into LDS
-  u32x4 vstage[kVChunks];
-  auto load_v = [&](int t) {
+  // K and V tiles -> registers with coalesced 16-byte loads, then -> LDS (V converted to
+  // fp16). Each step first writes the tile loaded during the previous step into the free
+  // LDS buffer and starts loading the one after it, then computes: the write latency and
+  // the load latency both hide under the compute, and nothing but LDS traffic is waited
+  // for at the barrier. Staging through registers measured faster here than the direct
+  // global->LDS load.
+  u32x4 ks[kVChunks], vs[kVChunks];
+  auto load_kv = [&](int t) {
     const int n0 = t * kBN;
 #pragma unroll
     for (int j = 0; j < kVChunks; ++j) {
-      const int ci = tid + kThreads * j;
+      const int ci = tid + kThr * j;
       const int row = ci / kCPR, ch = ci % kCPR;
-      vstage[j] = *reinterpret_cast<const u32x4*>(v + (size_t)min(n0 + row, N - 1) * D + ch * 8);
+      const size_t off = (size_t)min(n0 + row, N - 1) * D + ch * 8;
+      ks[j] = *reinterpret_cast<const u32x4*>(k + off);
+      vs[j] = *reinterpret_cast<const u32x4*>(v + off);
     }
   };
-  auto store_v = [&](FA_LDS uint8_t* vb) {
+  auto store_kv = [&](FA_LDS uint8_t* kb, FA_LDS uint8_t* vb) {
 #pragma unroll
     for (int j = 0; j < kVChunks; ++j) {
-      const int ci = tid + kThreads * j;
+      const int ci = tid + kThr * j;
       const int row = ci / kCPR, ch = ci % kCPR;
-      lds_write16(vb + tile_off<D>(row, ch), to_f16x8<T>(vstage[j]));
+      lds_write16(kb + tile_off<D>(row, ch), ks[j]);
+      lds_write16(vb + tile_off<D>(row, ch), to_f16x8<T>(vs[j]));
     }
   };
 
-  if (ntiles > 0) {
-    issue_k(0, (FA_LDS uint8_t*)Kb0);
-    load_v(0);
-  }
+  // loads are unconditional (clamped to the last tile) so the number in flight is the
+  // same on every path and the compiler only waits for the oldest ones
+  const int tlast = max(ntiles - 1, 0);
+  load_kv(0);
 
   // Q fragment: B operand of S^T = K Q^T, lane (qi, hh) holds Q[qrow][16c + 8hh + 0..7]
   u32x4 qf[kKC];
@@ -160,7 +161,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel_16(
       voff[r][db] = tile_off<D>(8 * hh + (gi >> 2) + 4 * r, db * 4 + 2 * (g & 1) + ((gi & 3) >> 1)) +
                     8 * (gi & 1);
 
-  if (ntiles > 0) store_v((FA_LDS uint8_t*)Vb0);
+  store_kv((FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Vb0);  // tile 0
+  load_kv(min(1, tlast));
 
   // S^T for the 32 keys of block `sub` of the tile in Ks
   auto scores = [&](const FA_LDS uint8_t* Ks, int sub) {
@@ -231,13 +233,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel_16(
   // vector units exponentiate block 0, and on P V of block 0 while they do block 1.
   auto step = [&](int t, const FA_LDS uint8_t* Ks, const FA_LDS uint8_t* Vs,
                   FA_LDS uint8_t* Kn, FA_LDS uint8_t* Vn) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const bool more = t + 1 < ntiles;
-    if (more) {
-      issue_k(t + 1, Kn);
-      load_v(t + 1);
-    }
+    barrier_lds();            // tile t visible; the other buffer (tile t-1) is free
+    store_kv(Kn, Vn);         // tile t+1 (clamped), loaded during the previous step
+    load_kv(min(t + 2, tlast));
     const int n0 = t * kBN;
     // a tile with no key visible to this wave is skipped; otherwise both 32-key blocks
     // run, and a block hidden from the whole wave is masked to -inf like any other
@@ -254,7 +252,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel_16(
       softmax_pv(s0, Vs, 0);
       softmax_pv(s1, Vs, 1);
     }
-    if (more) store_v(Vn);
   };
 
   for (int t = 0; t < ntiles; t += 2) {
@@ -438,25 +435,38 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel_f32(
 
 }  // namespace
 
-FwdGrid fwd_grid(int B, int H, int N) {
+// 8-wave workgroups when they still give at least one workgroup per CU
+static int fwd_waves(int B, int H, int N, int dtype) {
+  if (dtype == kDtypeF32) return 4;
+  const long long blocks8 = (long long)B * H * ((N + 255) / 256);
+  return blocks8 >= 256 ? 8 : 4;
+}
+
+FwdGrid fwd_grid(int B, int H, int N, int waves) {
   FwdGrid g;
-  g.n_mblk = (N + kBM - 1) / kBM;
+  g.n_mblk = (N + 32 * waves - 1) / (32 * waves);
   g.heads_per_xcd = (B * H + 7) / 8;
   g.blocks = 8 * g.heads_per_xcd * g.n_mblk;
   return g;
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-  const FwdGrid g = fwd_grid(a.B, a.H, a.N);
+  const int waves = fwd_waves(a.B, a.H, a.N, a.dtype);
+  const FwdGrid g = fwd_grid(a.B, a.H, a.N, waves);
   const auto* q16 = static_cast<const uint16_t*>(a.q);
   const auto* k16 = static_cast<const uint16_t*>(a.k);
   const auto* v16 = static_cast<const uint16_t*>(a.v);
   const float sl2 = a.scale * kLog2e;
   const int BH = a.B * a.H;
-#define FA_LAUNCH16(TAG, DIM)                                                              \
-  hipLaunchKernelGGL((fwd_kernel_16<TAG, DIM>), dim3(g.blocks), dim3(kThreads), 0, stream, \
-                     q16, k16, v16, a.o, a.lse, BH, a.H, a.N, a.scale, sl2, a.causal,      \
+#define FA_LAUNCH16W(TAG, DIM, WV)                                                        \
+  hipLaunchKernelGGL((fwd_kernel_16<TAG, DIM, WV>), dim3(g.blocks), dim3(WV * 64), 0, stream, \
+                     q16, k16, v16, a.o, a.lse, BH, a.H, a.N, a.scale, sl2, a.causal,       \
                      a.kv_len, g.n_mblk, g.heads_per_xcd)
+#define FA_LAUNCH16(TAG, DIM)                     \
+  do {                                            \
+    if (waves == 8) FA_LAUNCH16W(TAG, DIM, 8);    \
+    else FA_LAUNCH16W(TAG, DIM, 4);               \
+  } while (0)
 #define FA_LAUNCH32(DIM)                                                                  \
   hipLaunchKernelGGL((fwd_kernel_f32<DIM>), dim3(g.blocks), dim3(kThreads), 0, stream,    \
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k),       \
@@ -470,6 +480,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     if (a.d == 64) FA_LAUNCH32(64); else FA_LAUNCH32(128);
   }
 #undef FA_LAUNCH16
+#undef FA_LAUNCH16W
 #undef FA_LAUNCH32
   return hipGetLastError();
 }

@@ -29,7 +29,7 @@ struct FwdGrid {
   int blocks;
 };
 
-FwdGrid fwd_grid(int B, int H, int N);
+FwdGrid fwd_grid(int B, int H, int N, int waves);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 
 struct BwdArgs {

@@ -144,3 +144,21 @@ def test_fwd_on_side_stream():
         o, l = fa.fa_fwd(dev["q"], dev["k"], dev["v"], scale=inp["scale"])
     s.synchronize()
     assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,pad", [(False, False), (True, False), (False, True),
+                                       (True, True)])
+def test_fwd_wide_grid(d, causal, pad):
+    """Enough heads that the 256-row (8-wave) workgroups are used, with a ragged N."""
+    N = 300
+    w, inp = workloads.custom(8, 32, N, d, "bf16", causal, kv_range=(1, N) if pad else None,
+                              seed=31 + d, with_dout=False)
+    U.say(f"[fwd] wide grid N={N} d={d} causal={causal} pad={pad}")
+    o, lse = U.gpu_fwd(inp)
+    heads = [(b, h) for b in range(8) for h in range(32)]
+    ref = U.oracle_fwd(inp)
+    ro = np.stack([np.stack([ref[(b, h)][0] for h in range(32)]) for b in range(8)])
+    rl = np.stack([np.stack([ref[(b, h)][1] for h in range(32)]) for b in range(8)])
+    U.compare("O", o, ro, "bf16")
+    U.compare("LSE", lse, rl, "bf16")
