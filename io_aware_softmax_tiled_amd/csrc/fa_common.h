@@ -135,10 +135,15 @@ __device__ inline u32x2 lds_read_tr16(const FA_LDS uint8_t* p) {
 // memory clobber keeps the compiler from moving memory accesses across it.
 __device__ inline void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
-// lds_base + 16*l (lds_base wave-uniform).
-__device__ inline void global_to_lds16(const void* gptr, FA_LDS void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gptr, lds_base, 16, 0, 0);
+// Buffer resource over `bytes` bytes from `base` (wave-uniform): a load through it at
+// byte offset o >= bytes returns zeros instead of touching memory, so tiles that run
+// past the end of a sequence need no clamping, and moving to the next tile is scalar
+// arithmetic on the resource rather than per-lane address arithmetic.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)offset, 0, 0);
 }
 
 // XOR swizzle of 16-byte chunks inside a 16-bit-element tile row, so that

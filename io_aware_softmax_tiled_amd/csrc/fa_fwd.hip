@@ -1,7 +1,7 @@
-// Forward pass of exact attention on gfx950: one workgroup per block of 128 query rows
-// of one (batch, head); key/value tiles of 64 rows stream through LDS while the
-// online-softmax state (running maximum, running denominator, unnormalised output)
-// stays in registers, so the N x N scores never reach HBM.
+// Forward pass of exact attention on gfx950: one workgroup per block of query rows of
+// one (batch, head), 32 rows per wave; key/value tiles of 64 rows stream through LDS
+// while the online-softmax state (running maximum, running denominator, unnormalised
+// output) stays in registers, so the N x N scores never reach HBM.
 //
 // Method: "[Review] From Online Softmax to Flash Attention", Algorithm FlashAttention
 // (Tiling) -- per key tile: local maximum, new running maximum, denominator rescaled
@@ -20,21 +20,27 @@
 //   packed P feeds the P V product as its B operand with no data movement.
 // * O^T = V^T P^T takes V^T through the transposing LDS read, so V is staged in LDS
 //   row-major exactly like K.
-// * K and V tiles are staged global -> registers -> LDS one tile ahead (V converted
-//   to fp16 on the way) into an XOR-swizzled layout, double-buffered; each step writes
-//   the next tile and starts the load of the one after before computing, so load and
-//   write latency hide under the compute; one barrier per tile, which waits for LDS
-//   traffic only.
+// * K and V tiles are staged global -> registers -> LDS (V converted to fp16 on the
+//   way) into an XOR-swizzled layout with three buffers per tensor: the tile two ahead
+//   is written and the one three ahead is fetched while the current one is used, with
+//   one barrier per tile that waits for LDS traffic only. Loads go through buffer
+//   resources placed at the tile, so rows past the end of the sequence read as zeros.
+// * The key loop is software-pipelined over 32-key sub-blocks: the score product of the
+//   next sub-block (matrix cores) runs beside the exponentials of the current one
+//   (vector units), and the P V product beside the next row maximum; the LDS fragments
+//   of each product are read one region ahead. Scheduling hints interleave the streams.
 // * exp2 with scale*log2(e) folded into one FMA; the output is normalised once at the
 //   end (the pages normalise every step; the results are equal). The reference
-//   maximum used in the exponent is only raised when a tile's maximum exceeds it by
-//   more than 2^8 in the exponent, so most tiles skip the output rescale; the final
-//   division uses the same reference, so the result is unchanged.
-// * Causal masking is applied only on tiles that cross the diagonal, the key-padding
-//   bound or the end of the sequence; tiles past the diagonal or the padding are not
-//   visited at all, and 32-key halves that are fully masked for a wave are skipped.
+//   maximum used in the exponent is only raised when a sub-block's maximum exceeds it
+//   by more than 2^15 in the exponent (P stays inside fp16), so the output rescale is
+//   rare; the final division uses the same reference, so the result is unchanged.
+// * Masking touches only the sub-blocks that cross the diagonal, the key-padding bound
+//   or the end of the sequence for a wave; tiles past the workgroup's last visible key
+//   are not visited.
 // * Workgroups are ordered heaviest-first for causal attention, and all query blocks
 //   of a head are placed on one XCD so its K/V tiles are shared in that XCD's L2.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -65,12 +71,14 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   constexpr int kThr = W * 64;
   constexpr int kBMw = W * 32;                         // query rows per workgroup
   constexpr int kVChunks = kTileBytes / 16 / kThr;     // K/V chunks per thread per tile
-  // two buffers, as separate arrays so the compiler can tell the tile being read from
-  // the tile being filled
+  // three buffers per tensor, as separate arrays so the compiler can tell the tiles
+  // being read from the one being filled
   __shared__ __attribute__((aligned(1024))) uint8_t Kb0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t Kb1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t Kb2[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t Vb0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t Vb1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vb2[kTileBytes];
 
   const WgPos pos = wg_position(heads_per_xcd);
   if (pos.bh >= BH) return;
@@ -85,7 +93,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   if (kv_len != nullptr) kv_lim = min(N, max(1, kv_len[b]));
   const int m0 = mblk * kBMw;
   const int kend = causal ? min(kv_lim, m0 + kBMw) : kv_lim;
-  const int ntiles = (kend + kBN - 1) / kBN;
+  const int ntiles = (kend + kBN - 1) / kBN;  // >= 1: key 0 is always visible
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -97,21 +105,24 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   const int qrow_c = min(qrow, N - 1);
 
   // K and V tiles -> registers with coalesced 16-byte loads, then -> LDS (V converted to
-  // fp16). Each step first writes the tile loaded during the previous step into the free
-  // LDS buffer and starts loading the one after it, then computes: the write latency and
-  // the load latency both hide under the compute, and nothing but LDS traffic is waited
-  // for at the barrier. Staging through registers measured faster here than the direct
-  // global->LDS load.
+  // fp16), two tiles ahead of the one being computed. Loads go through a buffer resource
+  // that starts at the tile, so rows past the end of the sequence read as zeros.
   u32x4 ks[kVChunks], vs[kVChunks];
+  uint32_t ld_off[kVChunks];   // byte offset of this thread's chunks inside a tile
+#pragma unroll
+  for (int j = 0; j < kVChunks; ++j) {
+    const int ci = tid + kThr * j;
+    ld_off[j] = (uint32_t)((ci / kCPR) * D + (ci % kCPR) * 8) * 2;
+  }
   auto load_kv = [&](int t) {
     const int n0 = t * kBN;
+    const uint32_t bytes = (uint32_t)(N - n0) * D * 2;
+    const auto rk = buffer_rsrc(k + (size_t)n0 * D, bytes);
+    const auto rv = buffer_rsrc(v + (size_t)n0 * D, bytes);
 #pragma unroll
     for (int j = 0; j < kVChunks; ++j) {
-      const int ci = tid + kThr * j;
-      const int row = ci / kCPR, ch = ci % kCPR;
-      const size_t off = (size_t)min(n0 + row, N - 1) * D + ch * 8;
-      ks[j] = *reinterpret_cast<const u32x4*>(k + off);
-      vs[j] = *reinterpret_cast<const u32x4*>(v + off);
+      ks[j] = buffer_load16(rk, ld_off[j]);
+      vs[j] = buffer_load16(rv, ld_off[j]);
     }
   };
   auto store_kv = [&](FA_LDS uint8_t* kb, FA_LDS uint8_t* vb) {
@@ -123,10 +134,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
       lds_write16(vb + tile_off<D>(row, ch), to_f16x8<T>(vs[j]));
     }
   };
-
-  // loads are unconditional (clamped to the last tile) so the number in flight is the
-  // same on every path and the compiler only waits for the oldest ones
-  const int tlast = max(ntiles - 1, 0);
+  const int tlast = ntiles - 1;
   load_kv(0);
 
   // Q fragment: B operand of S^T = K Q^T, lane (qi, hh) holds Q[qrow][16c + 8hh + 0..7]
@@ -148,8 +156,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
 
   // Per-lane byte offsets inside a K or V tile, fixed for the whole loop. The swizzle
   // depends only on the low 4 bits of the row, so moving by 16 or 32 rows (and between
-  // the two buffers) is a compile-time constant the LDS instructions take as an
-  // immediate offset.
+  // buffers) is a compile-time constant the LDS instructions take as an immediate offset.
   int koff[kKC];
 #pragma unroll
   for (int c = 0; c < kKC; ++c) koff[c] = tile_off<D>(krow_base, 2 * c + hh);
@@ -163,27 +170,77 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
 
   store_kv((FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Vb0);  // tile 0
   load_kv(min(1, tlast));
+  store_kv((FA_LDS uint8_t*)Kb1, (FA_LDS uint8_t*)Vb1);  // tile 1 (clamped)
+  load_kv(min(2, tlast));
 
-  // S^T for the 32 keys of block `sub` of the tile in Ks
-  auto scores = [&](const FA_LDS uint8_t* Ks, int sub) {
+  // The key axis is walked in 32-key sub-blocks (the tiled recurrence with tile width
+  // 32), software-pipelined so each region pairs matrix-core work with vector work of
+  // the neighbouring sub-block, while the LDS fragments of the next region are read:
+  //   region A: scores of sub-block s+1 (MFMA) | P of sub-block s (exp, pack, sum)
+  //             | V fragments of sub-block s
+  //   region B: O^T += V^T P^T of sub-block s  | row maximum of sub-block s+1
+  //             | K fragments of sub-block s+2
+  // followed by the (rare) rescale for sub-block s+1. Hints interleave the streams
+  // inside each region so the vector units and the LDS work while the matrix cores do.
+  u32x4 kf[kKC];          // K fragments (A operand) of the next score product
+  u32x2 vf[2][kDB][2];    // V^T fragments (A operand) of the next P V product
+  auto read_k = [&](const FA_LDS uint8_t* Ks, int sub) {
+#pragma unroll
+    for (int c = 0; c < kKC; ++c) kf[c] = lds_read16(Ks + koff[c] + sub * 32 * D * 2);
+  };
+  auto read_v = [&](const FA_LDS uint8_t* Vs, int sub) {
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const int rows = (32 * sub + 16 * c2) * D * 2;
+        vf[c2][db][0] = lds_read_tr16(Vs + voff[0][db] + rows);
+        vf[c2][db][1] = lds_read_tr16(Vs + voff[1][db] + rows);
+      }
+  };
+  // S^T for 32 keys from the K fragments in kf
+  auto scores = [&]() {
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int c = 0; c < kKC; ++c)
-      acc = Mfma<T>::run(lds_read16(Ks + koff[c] + sub * 32 * D * 2), qf[c], acc);
+    for (int c = 0; c < kKC; ++c) acc = Mfma<T>::run(kf[c], qf[c], acc);
     return acc;
   };
-  // one online-softmax step over 32 keys (the tiled recurrence with tile width 32),
-  // then O^T += V^T P^T for those keys
-  auto softmax_pv = [&](f32x16 s, const FA_LDS uint8_t* Vs, int sub) {
+  // P = exp2(s*scale*log2e - m_ref*scale*log2e), rounded to fp16, and its row sum
+  auto expo = [&](const f32x16& s, uint32_t (&pk)[8]) {
+    const float nms = -m_ref * sl2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p0 = exp2_fast(fmaf(s[2 * i], sl2, nms));
+      const float p1 = exp2_fast(fmaf(s[2 * i + 1], sl2, nms));
+      pk[i] = Mfma<F16>::pack(p0, p1);
+      lsum = Mfma<F16>::dot_ones(pk[i], lsum);
+    }
+  };
+  // two 16-key steps of O^T += V^T P^T from the V^T fragments in vf
+  auto pv = [&](const uint32_t (&pk)[8]) {
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const u32x4 bp = {pk[4 * c2], pk[4 * c2 + 1], pk[4 * c2 + 2], pk[4 * c2 + 3]};
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+        oacc[db] = Mfma<F16>::run(u32x4{vf[c2][db][0][0], vf[c2][db][0][1],
+                                        vf[c2][db][1][0], vf[c2][db][1][1]},
+                                  bp, oacc[db]);
+    }
+  };
+  auto rowmax = [&](const f32x16& s) {
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[r], s[r + 1]);
-    mx = max_halves(mx);  // both halves of the wave hold the same query rows
-    // a row raises its reference maximum only when the exponent would exceed 2^8; the
-    // decision is per row, so each row's arithmetic depends on its own scores only
-    const bool grow = (mx - m_ref) * sl2 > 8.0f;
+    return max_halves(mx);  // both halves of the wave hold the same query rows
+  };
+  // a row raises its reference maximum only when the exponent would exceed 2^15 (P is
+  // then at most 2^15, inside fp16); the decision is per row, so each row's arithmetic
+  // depends on its own scores only
+  auto rescale = [&](float mx) {
+    const bool grow = (mx - m_ref) * sl2 > 15.0f;
     if (__any(grow)) {
       const float m_new = grow ? mx : m_ref;
       const float alpha = exp2_fast((m_ref - m_new) * sl2);  // 1 if kept, 0 from -inf
@@ -194,72 +251,103 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
     }
-    // P = exp2(s*scale*log2e - m_ref*scale*log2e), rounded to fp16, and its row sum
-    const float nms = -m_ref * sl2;
+  };
+  // -inf where a key of sub-block `sb` is hidden from this lane's query (diagonal,
+  // padding or sequence end); only sub-blocks that cross one of those bounds for this
+  // wave are touched. Register r holds key 32*sb + 8*hh + 16*(r/8) + r%8, so one
+  // per-lane bound (the last visible key, relative to the lane's first key) decides all
+  // sixteen.
+  const int last_vis = (causal ? min(kv_lim - 1, qrow) : kv_lim - 1) - 8 * hh;
+  auto mask = [&](f32x16& s, int sb) {
+    const int n0 = 32 * sb;
+    if ((n0 + 32 > kv_lim) || (causal && n0 + 31 > wq0)) {
+      const int lim = last_vis - n0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = (16 * (r >> 3) + (r & 7) > lim) ? -INFINITY : s[r];
+    }
+  };
+  // keeps P in the region that computes it (the compiler would otherwise sink it into
+  // the P V region, past the masking branch, and lose the overlap)
+  auto pin = [&](const uint32_t (&pk)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[i]));
+  };
+  // region A: each score MFMA followed by its share of the vector instructions (the 48
+  // of expo, plus those of the tile store when one is in the region) and of the V
+  // fragment reads
+  auto hint_a = [&](auto nvalu) {
+    constexpr int kPer = decltype(nvalu)::value / kKC;
+#pragma unroll
+    for (int c = 0; c < kKC; ++c) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, kPer, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * kDB / kKC, 0);
+    }
+  };
+  // region B: each P V MFMA followed by a K fragment read and a vector instruction of
+  // the row maximum
+  auto hint_b = [&]() {
+#pragma unroll
+    for (int c = 0; c < 2 * kDB; ++c) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, (kKC + 2 * kDB - 1) / (2 * kDB), 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+  };
+
+  barrier_lds();  // tiles 0 and 1 visible
+  read_k((const FA_LDS uint8_t*)Kb0, 0);
+  f32x16 S = scores();
+  mask(S, 0);
+  rescale(rowmax(S));
+  read_k((const FA_LDS uint8_t*)Kb0, 1);
+
+  // One key tile = two sub-blocks; tile t lives in buffers t%3. After the barrier that
+  // opens step t every wave is done with tile t-1, so tile t+2 (held in registers) is
+  // written into its buffers and tile t+3 is fetched. Every wave walks the whole tile
+  // range of the workgroup; sub-blocks past its own diagonal are masked (the one after
+  // the last tile is masked entirely).
+  auto step = [&](int t, const FA_LDS uint8_t* Ka, const FA_LDS uint8_t* Va,
+                  const FA_LDS uint8_t* Kn, FA_LDS uint8_t* Kw, FA_LDS uint8_t* Vw) {
+    barrier_lds();
+    store_kv(Kw, Vw);
+    load_kv(min(t + 3, tlast));
+
     uint32_t pk[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p0 = exp2_fast(fmaf(s[2 * i], sl2, nms));
-      const float p1 = exp2_fast(fmaf(s[2 * i + 1], sl2, nms));
-      pk[i] = Mfma<F16>::pack(p0, p1);
-      lsum = Mfma<F16>::dot_ones(pk[i], lsum);
-    }
-    // two 16-key steps; V^T through the transposing read
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      const u32x4 bp = {pk[4 * c2], pk[4 * c2 + 1], pk[4 * c2 + 2], pk[4 * c2 + 3]};
-      const int rows = (32 * sub + 16 * c2) * D * 2;
-#pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const u32x2 lo = lds_read_tr16(Vs + voff[0][db] + rows);
-        const u32x2 hi = lds_read_tr16(Vs + voff[1][db] + rows);
-        oacc[db] = Mfma<F16>::run(u32x4{lo[0], lo[1], hi[0], hi[1]}, bp, oacc[db]);
-      }
-    }
-  };
-  // -inf where key j is hidden from this lane's query (diagonal, padding or sequence end)
-  auto mask = [&](f32x16& s, int n0, int sub) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = n0 + 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
-      const bool hide = key >= kv_lim || (causal && key > qrow);
-      s[r] = hide ? -INFINITY : s[r];
-    }
+    f32x16 Sn = scores();        // sub-block 2t+1 (K fragments read beforehand)
+    expo(S, pk);                 // P of sub-block 2t
+    read_v(Va, 0);
+    hint_a(std::integral_constant<int, 48 + 12 * kVChunks + 12>{});  // with the V conversion and the load addresses
+    pin(pk);
+    mask(Sn, 2 * t + 1);
+    pv(pk);
+    float mx = rowmax(Sn);
+    read_k(Kn, 0);
+    hint_b();
+    rescale(mx);
+
+    S = scores();                // sub-block 2t+2
+    expo(Sn, pk);                // P of sub-block 2t+1
+    read_v(Va, 1);
+    hint_a(std::integral_constant<int, 48>{});
+    pin(pk);
+    mask(S, 2 * t + 2);
+    pv(pk);
+    mx = rowmax(S);
+    read_k(Kn, 1);
+    hint_b();
+    rescale(mx);
   };
 
-  // one tile: publish it (barrier), start fetching the next one into the other buffer,
-  // then run two 32-key online-softmax steps on it. Both blocks' score products are
-  // issued before the first softmax, so the matrix cores work on block 1 while the
-  // vector units exponentiate block 0, and on P V of block 0 while they do block 1.
-  auto step = [&](int t, const FA_LDS uint8_t* Ks, const FA_LDS uint8_t* Vs,
-                  FA_LDS uint8_t* Kn, FA_LDS uint8_t* Vn) {
-    barrier_lds();            // tile t visible; the other buffer (tile t-1) is free
-    store_kv(Kn, Vn);         // tile t+1 (clamped), loaded during the previous step
-    load_kv(min(t + 2, tlast));
-    const int n0 = t * kBN;
-    // a tile with no key visible to this wave is skipped; otherwise both 32-key blocks
-    // run, and a block hidden from the whole wave is masked to -inf like any other
-    // hidden key (so the code has one path and the accumulators are never copied)
-    const bool vis = (n0 < kv_lim) && (!causal || n0 <= wq0 + 31);
-    const bool need_mask = (n0 + kBN > kv_lim) || (causal && n0 + kBN - 1 > wq0);
-    if (vis) {
-      f32x16 s0 = scores(Ks, 0);
-      f32x16 s1 = scores(Ks, 1);
-      if (need_mask) {
-        mask(s0, n0, 0);
-        mask(s1, n0, 1);
-      }
-      softmax_pv(s0, Vs, 0);
-      softmax_pv(s1, Vs, 1);
-    }
-  };
-
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, (const FA_LDS uint8_t*)Kb0, (const FA_LDS uint8_t*)Vb0, (FA_LDS uint8_t*)Kb1,
-         (FA_LDS uint8_t*)Vb1);
+  for (int t = 0; t < ntiles; t += 3) {
+    step(t, (const FA_LDS uint8_t*)Kb0, (const FA_LDS uint8_t*)Vb0,
+         (const FA_LDS uint8_t*)Kb1, (FA_LDS uint8_t*)Kb2, (FA_LDS uint8_t*)Vb2);
     if (t + 1 < ntiles)
-      step(t + 1, (const FA_LDS uint8_t*)Kb1, (const FA_LDS uint8_t*)Vb1, (FA_LDS uint8_t*)Kb0,
-           (FA_LDS uint8_t*)Vb0);
+      step(t + 1, (const FA_LDS uint8_t*)Kb1, (const FA_LDS uint8_t*)Vb1,
+           (const FA_LDS uint8_t*)Kb2, (FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Vb0);
+    if (t + 2 < ntiles)
+      step(t + 2, (const FA_LDS uint8_t*)Kb2, (const FA_LDS uint8_t*)Vb2,
+           (const FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Kb1, (FA_LDS uint8_t*)Vb1);
   }
 
   // epilogue: O = O_acc / l, LSE = scale*m_ref + ln(l)
@@ -436,8 +524,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel_f32(
 }  // namespace
 
 // 8-wave workgroups when they still give at least one workgroup per CU
-static int fwd_waves(int B, int H, int N, int dtype) {
+static int fwd_waves(int B, int H, int N, int d, int dtype) {
   if (dtype == kDtypeF32) return 4;
+  if (d == 128) return 8;
   const long long blocks8 = (long long)B * H * ((N + 255) / 256);
   return blocks8 >= 256 ? 8 : 4;
 }
@@ -451,7 +540,7 @@ FwdGrid fwd_grid(int B, int H, int N, int waves) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-  const int waves = fwd_waves(a.B, a.H, a.N, a.dtype);
+  const int waves = fwd_waves(a.B, a.H, a.N, a.d, a.dtype);
   const FwdGrid g = fwd_grid(a.B, a.H, a.N, waves);
   const auto* q16 = static_cast<const uint16_t*>(a.q);
   const auto* k16 = static_cast<const uint16_t*>(a.k);
