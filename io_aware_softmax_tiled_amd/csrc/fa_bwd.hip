@@ -14,8 +14,9 @@
 //    on lanes. It loops over 64-query tiles (causal: from the block's diagonal on),
 //    recomputes S = Q K^T and dP = dO V^T, forms P and dS in registers, and accumulates
 //    dV^T += dO^T P and dK^T += Q^T dS in registers (dO^T and Q^T through the
-//    transposing LDS read). Q/dO tiles are prefetched one tile ahead and
-//    double-buffered: one barrier per tile.
+//    transposing LDS read). Q/dO tiles are prefetched one tile ahead through buffer
+//    resources and double-buffered: one barrier per tile, waiting for LDS traffic
+//    only.
 // 3. bwd_dq: one workgroup per 128 queries, 32 per wave, queries on lanes -- the
 //    forward kernel's layout. Per 64-key tile it recomputes S^T = K Q^T and
 //    dP^T = V dO^T, forms dS^T in registers and accumulates dQ^T += K^T dS^T (K^T
@@ -136,15 +137,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // staging of query tile `it` through registers (coalesced 16-byte loads)
   u32x4 qs[kSC], os[kSC];
   float s_lse = 0.f, s_dlt = 0.f;
+  // loads go through buffer resources placed at the tile: rows past the end of the
+  // sequence read as zeros, and moving to the next tile is scalar arithmetic
+  uint32_t ld_off[kSC];
+#pragma unroll
+  for (int j = 0; j < kSC; ++j) {
+    const int ci = tid + kThreads * j;
+    ld_off[j] = (uint32_t)((ci / kCPR) * D + (ci % kCPR) * 8) * 2;
+  }
   auto load_tile = [&](int it) {
     const int q0 = it * kBQ;
+    const uint32_t bytes = (uint32_t)(N - q0) * D * 2;
+    const auto rq = buffer_rsrc(Q + head + (size_t)q0 * D, bytes);
+    const auto ro = buffer_rsrc(dO + head + (size_t)q0 * D, bytes);
 #pragma unroll
     for (int j = 0; j < kSC; ++j) {
-      const int ci = tid + kThreads * j;
-      const int row = ci / kCPR, ch = ci % kCPR;
-      const size_t goff = head + (size_t)min(q0 + row, N - 1) * D + ch * 8;
-      qs[j] = *reinterpret_cast<const u32x4*>(Q + goff);
-      os[j] = *reinterpret_cast<const u32x4*>(dO + goff);
+      qs[j] = buffer_load16(rq, ld_off[j]);
+      os[j] = buffer_load16(ro, ld_off[j]);
     }
     if (tid < kBQ) {
       const size_t r = (size_t)bh * N + min(q0 + tid, N - 1);
@@ -280,10 +289,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   auto step = [&](int it, const FA_LDS uint8_t* Qc, const FA_LDS uint8_t* Oc,
                   const FA_LDS float* Stc, FA_LDS uint8_t* Qn, FA_LDS uint8_t* On,
                   FA_LDS float* Stn) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const bool more = it + 1 < nq;
-    if (more) load_tile(it + 1);
+    barrier_lds();  // tile `it` visible; the other buffers are free
+    load_tile(min(it + 1, nq - 1));  // unconditional: same loads in flight on every path
     const int q0 = it * kBQ;
     // a tile entirely above this wave's keys' diagonal (or a wave whose keys are all
     // padded) is skipped; otherwise both halves run, and a half hidden from every key is
@@ -302,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       accumulate(Qc, Oc, Stc, 0, s0, dp0);
       accumulate(Qc, Oc, Stc, 1, s1, dp1);
     }
-    if (more) store_tile(Qn, On, Stn);
+    store_tile(Qn, On, Stn);  // tile it+1 (clamped) into the free buffers
   };
 
   for (int it = i0; it < nq; it += 2) {
@@ -378,15 +385,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const int qrow_c = min(qrow, N - 1);
 
   u32x4 ks[kSC], vs[kSC];
+  uint32_t ld_off[kSC];
+#pragma unroll
+  for (int j = 0; j < kSC; ++j) {
+    const int ci = tid + kThreads * j;
+    ld_off[j] = (uint32_t)((ci / kCPR) * D + (ci % kCPR) * 8) * 2;
+  }
   auto load_tile = [&](int t) {
     const int n0 = t * kBN;
+    const uint32_t bytes = (uint32_t)(N - n0) * D * 2;
+    const auto rk = buffer_rsrc(K + head + (size_t)n0 * D, bytes);
+    const auto rv = buffer_rsrc(V + head + (size_t)n0 * D, bytes);
 #pragma unroll
     for (int j = 0; j < kSC; ++j) {
-      const int ci = tid + kThreads * j;
-      const int row = ci / kCPR, ch = ci % kCPR;
-      const size_t goff = head + (size_t)min(n0 + row, N - 1) * D + ch * 8;
-      ks[j] = *reinterpret_cast<const u32x4*>(K + goff);
-      vs[j] = *reinterpret_cast<const u32x4*>(V + goff);
+      ks[j] = buffer_load16(rk, ld_off[j]);
+      vs[j] = buffer_load16(rv, ld_off[j]);
     }
   };
   auto store_tile = [&](FA_LDS uint8_t* kb, FA_LDS uint8_t* vb) {
@@ -422,10 +435,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
   auto step = [&](int t, const FA_LDS uint8_t* Ks, const FA_LDS uint8_t* Vs, FA_LDS uint8_t* Kn,
                   FA_LDS uint8_t* Vn) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile(t + 1);
+    barrier_lds();  // tile t visible; the other buffers are free
+    load_tile(min(t + 1, ntiles - 1));  // unconditional: same loads in flight on every path
     const int n0 = t * kBN;
     const bool need_mask = (n0 + kBN > kv_lim) || (causal && n0 + kBN - 1 > wq0);
 #pragma unroll
@@ -477,7 +488,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         }
       }
     }
-    if (more) store_tile(Kn, Vn);
+    store_tile(Kn, Vn);  // tile t+1 (clamped) into the free buffers
   };
 
   for (int t = 0; t < ntiles; t += 2) {
