@@ -28,6 +28,8 @@
 // inputs are converted to fp16 when staged (exact for magnitudes in the fp16 normal
 // range); P and dS are rounded to fp16, whose 11-bit significand keeps dK and dQ well
 // inside the bf16 tolerance where bf16 rounding of dS would not.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -238,11 +240,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       s[r] = hide ? -INFINITY : s[r];
     }
   };
-  // P and dS for half `hf` (masked scores are -inf, so P = dS = 0 there), then
-  // dV^T += dO^T P and dK^T += Q^T dS
-  auto accumulate = [&](const FA_LDS uint8_t* Qc, const FA_LDS uint8_t* Oc, const FA_LDS float* Stc,
-                        int hf, const f32x16& s, const f32x16& dp) {
-    uint32_t pp[8], dsp[8];
+  // P and dS for half `hf` (masked scores are -inf, so P = dS = 0 there), packed fp16
+  auto p_ds = [&](const FA_LDS float* Stc, int hf, const f32x16& s, const f32x16& dp,
+                  uint32_t (&pp)[8], uint32_t (&dsp)[8]) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int qb = 32 * hf + 16 * c + 8 * hh;
@@ -266,6 +266,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         dsp[4 * c + j] = Mfma<F16>::pack(ds[2 * j], ds[2 * j + 1]);
       }
     }
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS for half `hf`
+  auto accumulate = [&](const FA_LDS uint8_t* Qc, const FA_LDS uint8_t* Oc, int hf,
+                        const uint32_t (&pp)[8], const uint32_t (&dsp)[8]) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const u32x4 bp = {pp[4 * c], pp[4 * c + 1], pp[4 * c + 2], pp[4 * c + 3]};
@@ -282,10 +286,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       }
     }
   };
+  // keeps P and dS in the region that computes them (the compiler would otherwise sink
+  // them past the masking branch into the product that uses them, losing the overlap)
+  auto pin = [&](const uint32_t (&pp)[8], const uint32_t (&dsp)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pp[i]), "v"(dsp[i]));
+  };
+  // each of the region's 4*kDB or 2*kKC MFMAs followed by its share of the ~90 vector
+  // instructions of p_ds and of the LDS reads
+  auto hint = [&](auto n_mfma, auto n_ds) {
+    constexpr int kM = decltype(n_mfma)::value;
+    constexpr int kDs = decltype(n_ds)::value;
+#pragma unroll
+    for (int i = 0; i < kM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, kDs / kM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, (96 + kM - 1) / kM, 0);
+    }
+  };
 
-  // one 64-query tile: publish it (barrier), prefetch the next one, issue the S and dP
-  // products of both halves, then finish half 0 (vector work overlapping half 1's
-  // products) and half 1.
+  // One 64-query tile: publish it (barrier), prefetch the next one, then (head_dim 64)
+  // three regions that keep the matrix cores busy while the vector units form P and dS:
+  //   products of half 0 | products of half 1 with P, dS of half 0 |
+  //   dV, dK products of half 0 with P, dS of half 1 | dV, dK products of half 1.
   auto step = [&](int it, const FA_LDS uint8_t* Qc, const FA_LDS uint8_t* Oc,
                   const FA_LDS float* Stc, FA_LDS uint8_t* Qn, FA_LDS uint8_t* On,
                   FA_LDS float* Stn) {
@@ -300,14 +323,36 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         (causal && kw0 + 31 > q0) || (q0 + kBQ > N) || (kw0 + 32 > kv_lim);
     if (active) {
       f32x16 s0, dp0, s1, dp1;
-      products(Qc, Oc, 0, s0, dp0);
-      products(Qc, Oc, 1, s1, dp1);
-      if (need_mask) {
-        mask(s0, q0, 0);
-        mask(s1, q0, 1);
+      uint32_t pp0[8], ds0[8], pp1[8], ds1[8];
+      if constexpr (D == 64) {
+        // three overlapped regions (see above)
+        products(Qc, Oc, 0, s0, dp0);
+        if (need_mask) mask(s0, q0, 0);
+        products(Qc, Oc, 1, s1, dp1);
+        p_ds(Stc, 0, s0, dp0, pp0, ds0);
+        hint(std::integral_constant<int, 2 * kKC>{}, std::integral_constant<int, 2 * kKC + 4>{});
+        pin(pp0, ds0);
+        if (need_mask) mask(s1, q0, 1);
+        accumulate(Qc, Oc, 0, pp0, ds0);
+        p_ds(Stc, 1, s1, dp1, pp1, ds1);
+        hint(std::integral_constant<int, 4 * kDB>{}, std::integral_constant<int, 8 * kDB + 4>{});
+        pin(pp1, ds1);
+        accumulate(Qc, Oc, 1, pp1, ds1);
+      } else {
+        // head_dim 128: both halves' products first, then P/dS and the dV/dK products
+        // per half, scheduled by the compiler (the overlapped regions measured slower
+        // here: twice the vector work per matrix product and the accumulators in AGPRs)
+        products(Qc, Oc, 0, s0, dp0);
+        products(Qc, Oc, 1, s1, dp1);
+        if (need_mask) {
+          mask(s0, q0, 0);
+          mask(s1, q0, 1);
+        }
+        p_ds(Stc, 0, s0, dp0, pp0, ds0);
+        accumulate(Qc, Oc, 0, pp0, ds0);
+        p_ds(Stc, 1, s1, dp1, pp1, ds1);
+        accumulate(Qc, Oc, 1, pp1, ds1);
       }
-      accumulate(Qc, Oc, Stc, 0, s0, dp0);
-      accumulate(Qc, Oc, Stc, 1, s1, dp1);
     }
     store_tile(Qn, On, Stn);  // tile it+1 (clamped) into the free buffers
   };
