@@ -13,6 +13,9 @@ page_algorithms   The softmax / attention recurrences the pages derive (3-pass s
                   softmax, 2-pass online softmax, 2-pass and 1-pass FlashAttention rows,
                   the tiled recurrence, the Br x Bc block update, the statistics merge),
                   written as scalar float64 loops. They cross-check the definition.
+split             Split-KV: attention over contiguous key ranges (normalised partial
+                  outputs with their LSE, empty rows O = 0, LSE = -inf) and the merge
+                  of partials by the incremental softmax tracking rule.
 
 Every function is pinned by tests in tests/test_oracle_*.py against closed forms,
 invariants, brute force, finite differences, independent library routines and
@@ -26,4 +29,11 @@ from .attention import (  # noqa: F401
     attention_backward,
     attention_forward_heads,
     attention_backward_heads,
+)
+from .split import (  # noqa: F401
+    split_ranges,
+    head_forward_range,
+    attention_forward_split,
+    merge_pair,
+    merge_partials,
 )
