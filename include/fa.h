@@ -106,6 +106,50 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const float* o,
            const int32_t* kv_len, void* workspace, size_t workspace_bytes,
            void* stream);
 
+/*
+ * Split-KV (key axis cut into ranges, partials merged afterwards).
+ * "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness"
+ * (summary of arXiv 2205.14135), Method, incremental softmax tracking: the softmax
+ * statistics of a vector split into parts combine as m = max(m1, m2),
+ * l = e^{m1-m} l1 + e^{m2-m} l2, and the block outputs are rescaled by the same
+ * factors. Computing each key range's block on its own and merging with this rule
+ * gives the unsplit result (up to rounding): more workgroups for few query rows and
+ * long key sequences, and the per-shard half of a sequence-parallel layout.
+ *
+ * fa_split_count: number of key ranges of split_len keys covering N keys,
+ * ceil(N / split_len); -1 when split_len is not a positive multiple of 64.
+ */
+FA_API int fa_split_count(int N, int split_len);
+
+/*
+ * Partial forward pass over key ranges. Range p holds keys
+ * [p*split_len, min(N, (p+1)*split_len)); visibility inside it is the usual one
+ * (causal, kv_len). For each range p and query row, writes the normalised partial
+ * output o_part[p] = P_p V over the range's visible keys and lse_part[p] = ln of the
+ * sum of exp over them; a row that sees no key of the range gets o_part = 0 and
+ * lse_part = -inf. o_part is float32 [n_splits, B, H, N, d], lse_part float32
+ * [n_splits, B, H, N], n_splits = fa_split_count(N, split_len); both caller-owned,
+ * 16- and 4-byte aligned, not overlapping the inputs or each other. split_len must
+ * be a positive multiple of 64 (FA_EINVAL otherwise). dtype FA_BF16 or FA_F16
+ * (FA_F32: FA_EUNSUPPORTED). Other arguments, limits and errors as fa_fwd.
+ */
+FA_API int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part,
+                   float* lse_part, int B, int H, int N, int d, float scale, int causal,
+                   int dtype, const int32_t* kv_len, int split_len, void* stream);
+
+/*
+ * Merge of n_splits partials (o_part [n_splits,B,H,N,d], lse_part [n_splits,B,H,N],
+ * float32, as fa_fwd_partial writes them) into o [B,H,N,d] and lse [B,H,N]:
+ *   m = max_p lse_part[p], lse = m + ln sum_p e^{lse_part[p] - m},
+ *   o = sum_p e^{lse_part[p] - lse} o_part[p];
+ * a row whose every lse_part is -inf gets o = 0, lse = -inf. Any partials with this
+ * meaning may be merged (for instance partials of key shards computed elsewhere).
+ * n_splits in [1, 65536]; d in {64, 128}; o_part/o 16-byte aligned, lse_part/lse
+ * 4-byte aligned; outputs must not overlap inputs or each other. Errors as fa_fwd.
+ */
+FA_API int fa_merge(const float* o_part, const float* lse_part, float* o, float* lse,
+             int n_splits, int B, int H, int N, int d, void* stream);
+
 /* Static description of a status code. */
 FA_API const char* fa_status_str(int status);
 

@@ -11,6 +11,10 @@ Functions have the C entry points' names:
     fa_fwd(q, k, v, *, causal=False, scale=None, kv_len=None) -> (o, lse)
     fa_bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, kv_len=None) -> (dq, dk, dv)
     fa_bwd_workspace_size(B, H, N, d) -> int
+    fa_split_count(N, split_len) -> int
+    fa_fwd_partial(q, k, v, *, split_len, causal=False, scale=None, kv_len=None)
+        -> (o_part [P,B,H,N,d], lse_part [P,B,H,N])
+    fa_merge(o_part, lse_part) -> (o, lse)
     fa_status_str(code) -> str, fa_last_error() -> str, fa_version() -> int
 Tensors are [B, H, N, d] contiguous (q, k, v, dout: float32, bfloat16 or float16;
 o, dq, dk, dv: float32), lse is [B, H, N] float32, kv_len an int32 [B] device tensor
@@ -24,8 +28,9 @@ import os
 
 import torch
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_str", "fa_last_error",
-           "fa_version", "FaError", "lib_path", "load_library",
+__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_split_count", "fa_fwd_partial",
+           "fa_merge", "fa_status_str", "fa_last_error", "fa_version", "FaError", "lib_path",
+           "load_library",
            "FA_F32", "FA_BF16", "FA_F16"]
 
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
@@ -63,6 +68,13 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd.restype = i32
     lib.fa_bwd_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_split_count.argtypes = [i32, i32]
+    lib.fa_split_count.restype = i32
+    lib.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, i32, vp,
+                                   i32, vp]
+    lib.fa_fwd_partial.restype = i32
+    lib.fa_merge.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.fa_merge.restype = i32
     lib.fa_status_str.argtypes = [i32]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -87,6 +99,10 @@ def fa_version() -> int:
 
 def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
     return int(load_library().fa_bwd_workspace_size(B, H, N, d))
+
+
+def fa_split_count(N: int, split_len: int) -> int:
+    return int(load_library().fa_split_count(N, split_len))
 
 
 def _check(status: int):
@@ -168,3 +184,49 @@ def fa_bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, kv_len=None, work
                         _stream(q.device, stream))
     _check(st)
     return dq, dk, dv
+
+
+def fa_fwd_partial(q, k, v, *, split_len, causal=False, scale=None, kv_len=None, out=None,
+                   lse=None, stream=None):
+    """Partial forward over key ranges of split_len keys (a multiple of 64): returns
+    (o_part float32 [P,B,H,N,d], lse_part float32 [P,B,H,N]), P = fa_split_count(N,
+    split_len). A row that sees no key of a range gets o_part = 0, lse_part = -inf."""
+    B, H, N, d = _shape(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    kv = _kv(kv_len, B, q.device)
+    P = fa_split_count(N, int(split_len))
+    if P < 0:
+        raise ValueError(f"split_len must be a positive multiple of 64 (got {split_len})")
+    o = (torch.empty((P, B, H, N, d), dtype=torch.float32, device=q.device)
+         if out is None else out)
+    lse_t = (torch.empty((P, B, H, N), dtype=torch.float32, device=q.device)
+             if lse is None else lse)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
+                                scale, int(bool(causal)), _DTYPE_CODE[q.dtype], _ptr(kv),
+                                int(split_len), _stream(q.device, stream))
+    _check(st)
+    return o, lse_t
+
+
+def fa_merge(o_part, lse_part, *, out=None, lse=None, stream=None):
+    """Merge partials (float32 [P,B,H,N,d] and [P,B,H,N]) into (o [B,H,N,d], lse [B,H,N])."""
+    if o_part.dim() != 5 or lse_part.dim() != 4 or tuple(lse_part.shape) != tuple(o_part.shape[:4]):
+        raise ValueError("o_part must be [P,B,H,N,d] and lse_part [P,B,H,N]")
+    if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
+        raise ValueError("partials are float32")
+    for t in (o_part, lse_part):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("partials must be contiguous GPU tensors")
+    P, B, H, N, d = (int(x) for x in o_part.shape)
+    o = (torch.empty((B, H, N, d), dtype=torch.float32, device=o_part.device)
+         if out is None else out)
+    lse_t = (torch.empty((B, H, N), dtype=torch.float32, device=o_part.device)
+             if lse is None else lse)
+    lib = load_library()
+    with torch.cuda.device(o_part.device):
+        st = lib.fa_merge(_ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse_t), P, B, H, N, d,
+                          _stream(o_part.device, stream))
+    _check(st)
+    return o, lse_t

@@ -111,6 +111,86 @@ int fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse, in
   return FA_OK;
 }
 
+int fa_split_count(int N, int split_len) {
+  if (split_len <= 0 || split_len % 64 != 0 || N < 0) return -1;
+  return (int)(((long long)N + split_len - 1) / split_len);
+}
+
+int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part,
+                   float* lse_part, int B, int H, int N, int d, float scale, int causal,
+                   int dtype, const int32_t* kv_len, int split_len, void* stream) {
+  clear_error();
+  int st = check_common(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (dtype == FA_F32)
+    return fail(FA_EUNSUPPORTED, "split-KV partials take bf16 or f16 inputs, not f32");
+  if (split_len <= 0 || split_len % 64 != 0)
+    return fail(FA_EINVAL, "split_len must be a positive multiple of 64 (got %d)", split_len);
+  if ((size_t)B * H * N == 0) return FA_OK;
+  if (!q || !k || !v || !o_part || !lse_part) return fail(FA_EINVAL, "null tensor pointer");
+  const int P = fa_split_count(N, split_len);
+  if ((double)P * B * H * N * d >= 1099511627776.0)
+    return fail(FA_EINVAL, "n_splits*B*H*N*d too large");
+  const double blocks = (double)P * 8.0 * std::ceil((double)B * H / 8.0) * std::ceil(N / 64.0);
+  if (blocks >= 2147483647.0) return fail(FA_EINVAL, "too many workgroups for one launch");
+  const size_t in_bytes = (size_t)B * H * N * d * elem_size(dtype);
+  const size_t o_bytes = (size_t)P * B * H * N * d * 4;
+  const size_t lse_bytes = (size_t)P * B * H * N * 4;
+  const Span ins[] = {{q, in_bytes, "q"}, {k, in_bytes, "k"}, {v, in_bytes, "v"},
+                      {kv_len, kv_len ? (size_t)B * 4 : 0, "kv_len"}};
+  const Span outs[] = {{o_part, o_bytes, "o_part"}, {lse_part, lse_bytes, "lse_part"}};
+  for (const Span& s : ins)
+    if (s.bytes && !aligned(s.p, s.p == kv_len ? 4 : 16))
+      return fail(FA_EINVAL, "%s is not %d-byte aligned", s.name, s.p == kv_len ? 4 : 16);
+  if (!aligned(o_part, 16)) return fail(FA_EINVAL, "o_part is not 16-byte aligned");
+  if (!aligned(lse_part, 4)) return fail(FA_EINVAL, "lse_part is not 4-byte aligned");
+  for (const Span& a : outs)
+    for (const Span& b : ins)
+      if (overlap(a, b)) return fail(FA_EINVAL, "output %s overlaps input %s", a.name, b.name);
+  if (overlap(outs[0], outs[1])) return fail(FA_EINVAL, "outputs o_part and lse_part overlap");
+
+  fa::FwdArgs a{q, k, v, o_part, lse_part, B, H, N, d, scale, causal ? 1 : 0, dtype, kv_len};
+  a.split_len = split_len;
+  hipError_t e = fa::launch_fwd(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(FA_EHIP, "partial forward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+int fa_merge(const float* o_part, const float* lse_part, float* o, float* lse, int n_splits,
+             int B, int H, int N, int d, void* stream) {
+  clear_error();
+  if (B < 0 || H < 0 || N < 0)
+    return fail(FA_EINVAL, "sizes must be >= 0 (B=%d H=%d N=%d)", B, H, N);
+  if (d != 64 && d != 128) return fail(FA_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", d);
+  if (n_splits < 1) return fail(FA_EINVAL, "n_splits must be >= 1 (got %d)", n_splits);
+  if (n_splits > 65536) return fail(FA_EINVAL, "n_splits=%d exceeds the limit 65536", n_splits);
+  if (N > (1 << 22)) return fail(FA_EINVAL, "N=%d exceeds the limit 2^22", N);
+  if ((double)n_splits * B * H * N * d >= 1099511627776.0)
+    return fail(FA_EINVAL, "n_splits*B*H*N*d too large");
+  if ((double)B * H * N * (d / 4) / 256.0 >= 2147483647.0)
+    return fail(FA_EINVAL, "too many workgroups for one launch");
+  if ((size_t)B * H * N == 0) return FA_OK;
+  if (!o_part || !lse_part || !o || !lse) return fail(FA_EINVAL, "null tensor pointer");
+  const size_t rows = (size_t)B * H * N;
+  const Span ins[] = {{o_part, (size_t)n_splits * rows * d * 4, "o_part"},
+                      {lse_part, (size_t)n_splits * rows * 4, "lse_part"}};
+  const Span outs[] = {{o, rows * d * 4, "o"}, {lse, rows * 4, "lse"}};
+  if (!aligned(o_part, 16) || !aligned(o, 16))
+    return fail(FA_EINVAL, "o_part and o must be 16-byte aligned");
+  if (!aligned(lse_part, 4) || !aligned(lse, 4))
+    return fail(FA_EINVAL, "lse_part and lse must be 4-byte aligned");
+  for (const Span& a : outs)
+    for (const Span& b : ins)
+      if (overlap(a, b)) return fail(FA_EINVAL, "output %s overlaps input %s", a.name, b.name);
+  if (overlap(outs[0], outs[1])) return fail(FA_EINVAL, "outputs o and lse overlap");
+
+  fa::MergeArgs a{o_part, lse_part, o, lse, n_splits, B, H, N, d};
+  hipError_t e = fa::launch_merge(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_EHIP, "merge launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
   return fa::bwd_workspace_bytes(B, H, N, d);

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) float St0[2 * kBQ];  // LSE*log2(e), then D
   __shared__ __attribute__((aligned(16))) float St1[2 * kBQ];
 
-  const WgPos pos = wg_position(heads_per_xcd);
+  const WgPos pos = wg_position(heads_per_xcd, blockIdx.x);
   const int kblk = pos.blk;  // key block 0 has the most query tiles under a causal mask
   if (pos.bh >= BH || kblk >= n_kblk) return;
   const int bh = pos.bh;
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t Vb0[kTile];
   __shared__ __attribute__((aligned(1024))) uint8_t Vb1[kTile];
 
-  const WgPos pos = wg_position(heads_per_xcd);
+  const WgPos pos = wg_position(heads_per_xcd, blockIdx.x);
   if (pos.bh >= BH) return;
   const int mblk = n_mblk - 1 - pos.blk;  // heaviest query block first
   const int bh = pos.bh;

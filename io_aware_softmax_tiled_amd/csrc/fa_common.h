@@ -91,8 +91,7 @@ __device__ inline int kappa(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8
 struct WgPos {
   int bh, blk;
 };
-__device__ inline WgPos wg_position(int heads_per_xcd) {
-  const int w = blockIdx.x;
+__device__ inline WgPos wg_position(int heads_per_xcd, int w) {
   const int xcd = w & 7;
   const int slot = w >> 3;
   return {(slot % heads_per_xcd) * 8 + xcd, slot / heads_per_xcd};

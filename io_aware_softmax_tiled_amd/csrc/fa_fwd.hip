@@ -58,12 +58,18 @@ constexpr int kThreads = 256;
 // W waves per workgroup (4 or 8), 32 query rows each. With 8 waves every K/V tile
 // loaded into LDS serves 256 query rows, halving the tile traffic per FLOP; 4 waves
 // keep enough workgroups for small problems.
-template <typename T, int D, int W>
+//
+// kPartial: split-KV. Workgroup index = split * per_split + (position as above); split p
+// covers keys [p*split_len, (p+1)*split_len) and writes its normalised partial output
+// and LSE at O + p*o_stride, LSE + p*lse_stride. A row that sees no key of its split
+// gets O = 0 and LSE = -inf.
+template <typename T, int D, int W, bool kPartial>
 __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
     int BH, int H, int N, float scale, float sl2, int causal,
-    const int* __restrict__ kv_len, int n_mblk, int heads_per_xcd) {
+    const int* __restrict__ kv_len, int n_mblk, int heads_per_xcd, int split_len,
+    int per_split, size_t o_stride, size_t lse_stride) {
   constexpr int kTileBytes = kBN * D * 2;              // one K or V tile
   constexpr int kKC = D / 16;                          // 16-wide k-steps over head_dim
   constexpr int kDB = D / 32;                          // 32-row blocks of O^T
@@ -80,7 +86,12 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   __shared__ __attribute__((aligned(1024))) uint8_t Vb1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t Vb2[kTileBytes];
 
-  const WgPos pos = wg_position(heads_per_xcd);
+  int split = 0, wid = blockIdx.x;
+  if constexpr (kPartial) {
+    split = blockIdx.x / per_split;
+    wid = blockIdx.x - split * per_split;
+  }
+  const WgPos pos = wg_position(heads_per_xcd, wid);
   if (pos.bh >= BH) return;
   const int mblk = n_mblk - 1 - pos.blk;  // heaviest query block first
   const int b = pos.bh / H;
@@ -88,12 +99,21 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   const uint16_t* q = Q + head;
   const uint16_t* k = K + head;
   const uint16_t* v = V + head;
+  if constexpr (kPartial) {
+    O += split * o_stride;
+    LSE += split * lse_stride;
+  }
 
   int kv_lim = N;
   if (kv_len != nullptr) kv_lim = min(N, max(1, kv_len[b]));
   const int m0 = mblk * kBMw;
-  const int kend = causal ? min(kv_lim, m0 + kBMw) : kv_lim;
-  const int ntiles = (kend + kBN - 1) / kBN;  // >= 1: key 0 is always visible
+  // keys [kbeg, kv_hi) of this workgroup's range can be visible: all of them, or one
+  // split's range (its first key is a tile boundary)
+  const int kbeg = kPartial ? split * split_len : 0;
+  const int kv_hi = kPartial ? min(kv_lim, kbeg + split_len) : kv_lim;
+  const int kend = causal ? min(kv_hi, m0 + kBMw) : kv_hi;
+  // >= 1 without a split (key 0 is always visible); a split may hold no visible key
+  const int ntiles = kend > kbeg ? (kend - kbeg + kBN - 1) / kBN : 0;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,6 +123,19 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   const int wq0 = m0 + wave * 32;              // first query row of this wave
   const int qrow = wq0 + qi;
   const int qrow_c = min(qrow, N - 1);
+
+  if constexpr (kPartial) {
+    if (ntiles == 0) {  // no key of the split is visible to this block: empty partials
+      if (qrow < N) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        float* orow = O + head + (size_t)qrow * D;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) *reinterpret_cast<f32x4*>(orow + 8 * c + 4 * hh) = z;
+        if (hh == 0) LSE[(size_t)pos.bh * N + qrow] = -INFINITY;
+      }
+      return;
+    }
+  }
 
   // K and V tiles -> registers with coalesced 16-byte loads, then -> LDS (V converted to
   // fp16), two tiles ahead of the one being computed. Loads go through a buffer resource
@@ -115,7 +148,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
     ld_off[j] = (uint32_t)((ci / kCPR) * D + (ci % kCPR) * 8) * 2;
   }
   auto load_kv = [&](int t) {
-    const int n0 = t * kBN;
+    const int n0 = kbeg + t * kBN;
     const uint32_t bytes = (uint32_t)(N - n0) * D * 2;
     const auto rk = buffer_rsrc(k + (size_t)n0 * D, bytes);
     const auto rv = buffer_rsrc(v + (size_t)n0 * D, bytes);
@@ -209,7 +242,9 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   };
   // P = exp2(s*scale*log2e - m_ref*scale*log2e), rounded to fp16, and its row sum
   auto expo = [&](const f32x16& s, uint32_t (&pk)[8]) {
-    const float nms = -m_ref * sl2;
+    // (a row that has seen no visible key yet -- possible only in a split -- keeps
+    // m_ref = -inf; its scores are all -inf and must give P = 0, not NaN)
+    const float nms = (kPartial && m_ref == -INFINITY) ? 0.f : -m_ref * sl2;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float p0 = exp2_fast(fmaf(s[2 * i], sl2, nms));
@@ -257,10 +292,10 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   // wave are touched. Register r holds key 32*sb + 8*hh + 16*(r/8) + r%8, so one
   // per-lane bound (the last visible key, relative to the lane's first key) decides all
   // sixteen.
-  const int last_vis = (causal ? min(kv_lim - 1, qrow) : kv_lim - 1) - 8 * hh;
+  const int last_vis = (causal ? min(kv_hi - 1, qrow) : kv_hi - 1) - 8 * hh;
   auto mask = [&](f32x16& s, int sb) {
-    const int n0 = 32 * sb;
-    if ((n0 + 32 > kv_lim) || (causal && n0 + 31 > wq0)) {
+    const int n0 = kbeg + 32 * sb;
+    if ((n0 + 32 > kv_hi) || (causal && n0 + 31 > wq0)) {
       const int lim = last_vis - n0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = (16 * (r >> 3) + (r & 7) > lim) ? -INFINITY : s[r];
@@ -353,7 +388,9 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   // epilogue: O = O_acc / l, LSE = scale*m_ref + ln(l)
   const float ltot = sum_halves(lsum);
   if (qrow < N) {
-    const float inv = 1.0f / ltot;
+    // a row with no visible key in its split (ltot = 0) gets O = 0, LSE = -inf
+    const bool empty = kPartial && !(ltot > 0.f);
+    const float inv = empty ? 0.f : 1.0f / ltot;
     float* orow = O + head + (size_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
@@ -363,7 +400,9 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
                            oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv};
         *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * a4 + 4 * hh) = val;
       }
-    if (hh == 0) LSE[(size_t)pos.bh * N + qrow] = m_ref * scale + log2_fast(ltot) * kLn2;
+    if (hh == 0)
+      LSE[(size_t)pos.bh * N + qrow] =
+          empty ? -INFINITY : m_ref * scale + log2_fast(ltot) * kLn2;
   }
 }
 
@@ -380,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel_f32(
   __shared__ __attribute__((aligned(16))) float Ks[kBN * kLd];
   __shared__ __attribute__((aligned(16))) float Vs[kBN * kLd];
 
-  const WgPos pos = wg_position(heads_per_xcd);
+  const WgPos pos = wg_position(heads_per_xcd, blockIdx.x);
   if (pos.bh >= BH) return;
   const int mblk = n_mblk - 1 - pos.blk;  // heaviest query block first
   const int b = pos.bh / H;
@@ -547,14 +586,24 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   const auto* v16 = static_cast<const uint16_t*>(a.v);
   const float sl2 = a.scale * kLog2e;
   const int BH = a.B * a.H;
-#define FA_LAUNCH16W(TAG, DIM, WV)                                                        \
-  hipLaunchKernelGGL((fwd_kernel_16<TAG, DIM, WV>), dim3(g.blocks), dim3(WV * 64), 0, stream, \
-                     q16, k16, v16, a.o, a.lse, BH, a.H, a.N, a.scale, sl2, a.causal,       \
-                     a.kv_len, g.n_mblk, g.heads_per_xcd)
-#define FA_LAUNCH16(TAG, DIM)                     \
-  do {                                            \
-    if (waves == 8) FA_LAUNCH16W(TAG, DIM, 8);    \
-    else FA_LAUNCH16W(TAG, DIM, 4);               \
+  const bool partial = a.split_len > 0;
+  const int n_splits = partial ? (a.N + a.split_len - 1) / a.split_len : 1;
+  const size_t o_stride = (size_t)BH * a.N * a.d, lse_stride = (size_t)BH * a.N;
+#define FA_LAUNCH16W(TAG, DIM, WV, PART)                                                   \
+  hipLaunchKernelGGL((fwd_kernel_16<TAG, DIM, WV, PART>), dim3(g.blocks * n_splits),        \
+                     dim3(WV * 64), 0, stream, q16, k16, v16, a.o, a.lse, BH, a.H, a.N,     \
+                     a.scale, sl2, a.causal, a.kv_len, g.n_mblk, g.heads_per_xcd,           \
+                     a.split_len, g.blocks, o_stride, lse_stride)
+  // head_dim 128 always runs 8 waves (its LDS use allows one workgroup per CU)
+#define FA_LAUNCH16(TAG, DIM, PART)                                 \
+  do {                                                              \
+    if (DIM == 128 || waves == 8) FA_LAUNCH16W(TAG, DIM, 8, PART);  \
+    else FA_LAUNCH16W(TAG, 64, 4, PART);                            \
+  } while (0)
+#define FA_LAUNCH16P(TAG, DIM)                       \
+  do {                                               \
+    if (partial) FA_LAUNCH16(TAG, DIM, true);        \
+    else FA_LAUNCH16(TAG, DIM, false);               \
   } while (0)
 #define FA_LAUNCH32(DIM)                                                                  \
   hipLaunchKernelGGL((fwd_kernel_f32<DIM>), dim3(g.blocks), dim3(kThreads), 0, stream,    \
@@ -562,12 +611,14 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
                      static_cast<const float*>(a.v), a.o, a.lse, BH, a.H, a.N, a.scale, sl2, \
                      a.causal, a.kv_len, g.n_mblk, g.heads_per_xcd)
   if (a.dtype == kDtypeBF16) {
-    if (a.d == 64) FA_LAUNCH16(BF16, 64); else FA_LAUNCH16(BF16, 128);
+    if (a.d == 64) FA_LAUNCH16P(BF16, 64); else FA_LAUNCH16P(BF16, 128);
   } else if (a.dtype == kDtypeF16) {
-    if (a.d == 64) FA_LAUNCH16(F16, 64); else FA_LAUNCH16(F16, 128);
+    if (a.d == 64) FA_LAUNCH16P(F16, 64); else FA_LAUNCH16P(F16, 128);
   } else {
+    if (partial) return hipErrorNotSupported;  // rejected by the API layer
     if (a.d == 64) FA_LAUNCH32(64); else FA_LAUNCH32(128);
   }
+#undef FA_LAUNCH16P
 #undef FA_LAUNCH16
 #undef FA_LAUNCH16W
 #undef FA_LAUNCH32

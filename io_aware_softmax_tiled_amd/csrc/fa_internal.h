@@ -21,6 +21,9 @@ struct FwdArgs {
   int causal;
   int dtype;
   const int* kv_len;
+  // split-KV: keys per split (a multiple of 64), 0 for none. With a split, o and lse
+  // point at [n_splits, B, H, N, d] and [n_splits, B, H, N] partial outputs.
+  int split_len = 0;
 };
 
 struct FwdGrid {
@@ -51,6 +54,15 @@ struct BwdArgs {
 };
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
+
+struct MergeArgs {
+  const float* o_part;    // [n_splits, B, H, N, d]
+  const float* lse_part;  // [n_splits, B, H, N]
+  float* o;               // [B, H, N, d]
+  float* lse;             // [B, H, N]
+  int n_splits, B, H, N, d;
+};
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace fa

@@ -31,7 +31,8 @@ def lib():
 
 def test_header_declares_the_api():
     assert declared_symbols() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd",
-                                  "fa_last_error", "fa_status_str", "fa_version"]
+                                  "fa_fwd_partial", "fa_last_error", "fa_merge",
+                                  "fa_split_count", "fa_status_str", "fa_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -133,3 +134,69 @@ def test_python_binding_requires_gpu_tensors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fa_fwd(q, q, q)
+
+
+# ---- split-KV partials and merge -----------------------------------------------------
+
+def test_split_count(lib):
+    assert fa.fa_split_count(4096, 1024) == 4
+    assert fa.fa_split_count(4097, 1024) == 5
+    assert fa.fa_split_count(64, 4096) == 1
+    assert fa.fa_split_count(0, 64) == 0
+    assert fa.fa_split_count(100, 0) == -1
+    assert fa.fa_split_count(100, 96) == -1      # not a multiple of 64
+    assert fa.fa_split_count(100, -64) == -1
+
+
+def _part(lib, q=P, k=P + 0x100000, v=P + 0x200000, o=P + 0x300000, lse=P + 0x700000,
+          B=1, H=1, N=256, d=64, scale=0.125, causal=0, dtype=1, kv=None, split_len=64):
+    return lib.fa_fwd_partial(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, kv,
+                              split_len, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(split_len=0), FA_EINVAL),
+    (dict(split_len=96), FA_EINVAL),
+    (dict(split_len=-64), FA_EINVAL),
+    (dict(dtype=0), FA_EUNSUPPORTED),      # no fp32 partials
+    (dict(d=32), FA_EUNSUPPORTED),
+    (dict(o=None), FA_EINVAL),
+    (dict(o=P + 8), FA_EINVAL),
+    (dict(lse=P + 0x700002), FA_EINVAL),
+    (dict(o=P + 0x200000), FA_EINVAL),     # o_part overlaps v
+    (dict(lse=P + 0x300000 + 4096), FA_EINVAL),  # lse_part inside o_part (4 splits)
+    (dict(scale=float("nan")), FA_EINVAL),
+])
+def test_partial_rejects_before_launch(lib, kw, code):
+    assert _part(lib, **kw) == code
+    assert fa.fa_last_error() != ""
+
+
+def test_partial_empty_is_noop(lib):
+    assert _part(lib, N=0) == FA_OK
+    assert _part(lib, B=0, q=None) == FA_OK
+
+
+def _merge(lib, op=P, lp=P + 0x400000, o=P + 0x500000, lse=P + 0x600000, n=4, B=1, H=1,
+           N=256, d=64):
+    return lib.fa_merge(op, lp, o, lse, n, B, H, N, d, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), FA_EINVAL),
+    (dict(n=65537), FA_EINVAL),
+    (dict(d=96), FA_EUNSUPPORTED),
+    (dict(N=-1), FA_EINVAL),
+    (dict(op=None), FA_EINVAL),
+    (dict(o=P + 8), FA_EINVAL),
+    (dict(lse=P + 0x600002), FA_EINVAL),
+    (dict(o=P + 0x1000), FA_EINVAL),       # o overlaps o_part
+    (dict(lse=P + 0x500000 + 64), FA_EINVAL),  # lse inside o
+])
+def test_merge_rejects_before_launch(lib, kw, code):
+    assert _merge(lib, **kw) == code
+    assert fa.fa_last_error() != ""
+
+
+def test_merge_empty_is_noop(lib):
+    assert _merge(lib, N=0) == FA_OK
