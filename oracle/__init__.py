@@ -16,6 +16,8 @@ page_algorithms   The softmax / attention recurrences the pages derive (3-pass s
 split             Split-KV: attention over contiguous key ranges (normalised partial
                   outputs with their LSE, empty rows O = 0, LSE = -inf) and the merge
                   of partials by the incremental softmax tracking rule.
+sparse            Block-sparse attention: the definition with a block mask over
+                  query/key blocks (empty rows O = 0, LSE = -inf) and its gradient.
 
 Every function is pinned by tests in tests/test_oracle_*.py against closed forms,
 invariants, brute force, finite differences, independent library routines and
@@ -29,6 +31,13 @@ from .attention import (  # noqa: F401
     attention_backward,
     attention_forward_heads,
     attention_backward_heads,
+)
+from .sparse import (  # noqa: F401
+    block_allowed,
+    head_forward_sparse,
+    head_backward_sparse,
+    attention_forward_sparse,
+    attention_backward_sparse,
 )
 from .split import (  # noqa: F401
     split_ranges,
