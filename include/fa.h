@@ -150,6 +150,35 @@ FA_API int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_
 FA_API int fa_merge(const float* o_part, const float* lse_part, float* o, float* lse,
              int n_splits, int B, int H, int N, int d, void* stream);
 
+/*
+ * Block-sparse attention.
+ * "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness"
+ * (summary of arXiv 2205.14135), Extension: Block-Sparse FlashAttention: with a fixed
+ * sparsity mask M in {0,1}^{(N/Br) x (N/Bc)} only the nonzero blocks are evaluated, and
+ * the HBM traffic falls with the fraction s of nonzero blocks. Here Br = Bc =
+ * FA_SPARSE_BLOCK and block_mask is a device array of ceil(N/128)^2 bytes, row-major
+ * [query block][key block], shared by every batch and head; a zero entry hides every
+ * key of that key block from every query of that query block, on top of the causal and
+ * kv_len rules. The result equals dense attention with those scores set to -inf; a
+ * query row that sees no key at all gets o = 0 and lse = -inf (and zero gradients).
+ * Zero blocks are skipped: their K/V (forward, dq) or Q/dO (dk/dv) tiles are neither
+ * loaded nor multiplied. N <= FA_SPARSE_MAX_N; dtype FA_BF16 or FA_F16; other
+ * arguments, layouts and errors as fa_fwd / fa_bwd (o and lse passed to fa_bwd_sparse
+ * come from fa_fwd_sparse with the same mask).
+ */
+#define FA_SPARSE_BLOCK 128
+#define FA_SPARSE_MAX_N (1 << 20)
+
+FA_API int fa_fwd_sparse(const void* q, const void* k, const void* v, float* o, float* lse,
+                  int B, int H, int N, int d, float scale, int causal, int dtype,
+                  const int32_t* kv_len, const uint8_t* block_mask, void* stream);
+
+FA_API int fa_bwd_sparse(const void* q, const void* k, const void* v, const float* o,
+                  const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                  int B, int H, int N, int d, float scale, int causal, int dtype,
+                  const int32_t* kv_len, const uint8_t* block_mask, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 FA_API const char* fa_status_str(int status);
 

@@ -15,6 +15,8 @@ Functions have the C entry points' names:
     fa_fwd_partial(q, k, v, *, split_len, causal=False, scale=None, kv_len=None)
         -> (o_part [P,B,H,N,d], lse_part [P,B,H,N])
     fa_merge(o_part, lse_part) -> (o, lse)
+    fa_fwd_sparse(q, k, v, block_mask, *, causal=False, scale=None, kv_len=None) -> (o, lse)
+    fa_bwd_sparse(q, k, v, o, dout, lse, block_mask, *, ...) -> (dq, dk, dv)
     fa_status_str(code) -> str, fa_last_error() -> str, fa_version() -> int
 Tensors are [B, H, N, d] contiguous (q, k, v, dout: float32, bfloat16 or float16;
 o, dq, dk, dv: float32), lse is [B, H, N] float32, kv_len an int32 [B] device tensor
@@ -29,11 +31,12 @@ import os
 import torch
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_split_count", "fa_fwd_partial",
-           "fa_merge", "fa_status_str", "fa_last_error", "fa_version", "FaError", "lib_path",
+           "fa_merge", "fa_fwd_sparse", "fa_bwd_sparse", "FA_SPARSE_BLOCK", "fa_status_str", "fa_last_error", "fa_version", "FaError", "lib_path",
            "load_library",
            "FA_F32", "FA_BF16", "FA_F16"]
 
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
+FA_SPARSE_BLOCK = 128
 _DTYPE_CODE = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.float16: FA_F16}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -75,6 +78,12 @@ def load_library() -> ctypes.CDLL:
     lib.fa_fwd_partial.restype = i32
     lib.fa_merge.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.fa_merge.restype = i32
+    lib.fa_fwd_sparse.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, i32, vp,
+                                  vp, vp]
+    lib.fa_fwd_sparse.restype = i32
+    lib.fa_bwd_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                  i32, i32, vp, vp, vp, sz, vp]
+    lib.fa_bwd_sparse.restype = i32
     lib.fa_status_str.argtypes = [i32]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -230,3 +239,59 @@ def fa_merge(o_part, lse_part, *, out=None, lse=None, stream=None):
                           _stream(o_part.device, stream))
     _check(st)
     return o, lse_t
+
+
+def _mask(block_mask, N, device):
+    nb = -(-N // FA_SPARSE_BLOCK)
+    if block_mask.dtype != torch.uint8 or tuple(block_mask.shape) != (nb, nb):
+        raise ValueError(f"block_mask must be a uint8 [{nb}, {nb}] tensor")
+    if block_mask.device != device or not block_mask.is_contiguous():
+        raise ValueError("block_mask must be contiguous on the inputs' device")
+    return block_mask
+
+
+def fa_fwd_sparse(q, k, v, block_mask, *, causal=False, scale=None, kv_len=None, out=None,
+                  lse=None, stream=None):
+    """Block-sparse forward: block_mask uint8 [ceil(N/128), ceil(N/128)] (nonzero =
+    evaluated); returns (o, lse) with o = 0, lse = -inf on rows that see no key."""
+    B, H, N, d = _shape(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    kv = _kv(kv_len, B, q.device)
+    bm = _mask(block_mask, N, q.device)
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
+                               scale, int(bool(causal)), _DTYPE_CODE[q.dtype], _ptr(kv),
+                               _ptr(bm), _stream(q.device, stream))
+    _check(st)
+    return o, lse_t
+
+
+def fa_bwd_sparse(q, k, v, o, dout, lse, block_mask, *, causal=False, scale=None,
+                  kv_len=None, workspace=None, stream=None):
+    """Block-sparse backward of sum(dout * O): returns (dq, dk, dv), float32 [B,H,N,d]."""
+    B, H, N, d = _shape(q, k, v)
+    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
+        raise ValueError("dout must match q in shape and dtype and be contiguous")
+    if o.dtype != torch.float32 or lse.dtype != torch.float32:
+        raise ValueError("o and lse must be the float32 outputs of fa_fwd_sparse")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    kv = _kv(kv_len, B, q.device)
+    bm = _mask(block_mask, N, q.device)
+    ws_bytes = fa_bwd_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa_bwd_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                               _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, scale,
+                               int(bool(causal)), _DTYPE_CODE[q.dtype], _ptr(kv), _ptr(bm),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(q.device, stream))
+    _check(st)
+    return dq, dk, dv

@@ -80,9 +80,27 @@ const char* fa_last_error(void) { return g_last_error; }
 
 int fa_version(void) { return 100; /* 0.1.0 */ }
 
-int fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
-           int N, int d, float scale, int causal, int dtype, const int32_t* kv_len,
-           void* stream) {
+}  // extern "C"
+
+namespace {
+
+size_t sparse_mask_bytes(int N) {
+  const size_t n_sb = ((size_t)N + FA_SPARSE_BLOCK - 1) / FA_SPARSE_BLOCK;
+  return n_sb * n_sb;
+}
+
+int check_sparse(int N, int dtype, const uint8_t* block_mask) {
+  if (dtype == FA_F32)
+    return fail(FA_EUNSUPPORTED, "block-sparse attention takes bf16 or f16 inputs, not f32");
+  if (N > FA_SPARSE_MAX_N)
+    return fail(FA_EINVAL, "N=%d exceeds the block-sparse limit %d", N, FA_SPARSE_MAX_N);
+  if (N > 0 && !block_mask) return fail(FA_EINVAL, "null block_mask");
+  return FA_OK;
+}
+
+int fwd_impl(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
+             int N, int d, float scale, int causal, int dtype, const int32_t* kv_len,
+             const uint8_t* block_mask, void* stream) {
   clear_error();
   int st = check_common(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
@@ -92,11 +110,13 @@ int fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse, in
   const size_t o_bytes = (size_t)B * H * N * d * 4;
   const size_t lse_bytes = (size_t)B * H * N * 4;
   const Span ins[] = {{q, in_bytes, "q"}, {k, in_bytes, "k"}, {v, in_bytes, "v"},
-                      {kv_len, kv_len ? (size_t)B * 4 : 0, "kv_len"}};
+                      {kv_len, kv_len ? (size_t)B * 4 : 0, "kv_len"},
+                      {block_mask, block_mask ? sparse_mask_bytes(N) : 0, "block_mask"}};
   const Span outs[] = {{o, o_bytes, "o"}, {lse, lse_bytes, "lse"}};
-  for (const Span& s : ins)
-    if (s.bytes && !aligned(s.p, s.p == kv_len ? 4 : 16))
-      return fail(FA_EINVAL, "%s is not %d-byte aligned", s.name, s.p == kv_len ? 4 : 16);
+  for (const Span& s : ins) {
+    const size_t al = s.p == kv_len ? 4 : s.p == block_mask ? 1 : 16;
+    if (s.bytes && !aligned(s.p, al)) return fail(FA_EINVAL, "%s is not %zu-byte aligned", s.name, al);
+  }
   if (!aligned(o, 16)) return fail(FA_EINVAL, "o is not 16-byte aligned");
   if (!aligned(lse, 4)) return fail(FA_EINVAL, "lse is not 4-byte aligned");
   for (const Span& a : outs) {
@@ -106,9 +126,32 @@ int fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse, in
   if (overlap(outs[0], outs[1])) return fail(FA_EINVAL, "outputs o and lse overlap");
 
   fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal ? 1 : 0, dtype, kv_len};
+  a.block_mask = block_mask;
   hipError_t e = fa::launch_fwd(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_EHIP, "forward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
+           int N, int d, float scale, int causal, int dtype, const int32_t* kv_len,
+           void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, kv_len, nullptr, stream);
+}
+
+int fa_fwd_sparse(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                  int H, int N, int d, float scale, int causal, int dtype,
+                  const int32_t* kv_len, const uint8_t* block_mask, void* stream) {
+  clear_error();
+  int st = check_common(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  st = check_sparse(N, dtype, block_mask);
+  if (st != FA_OK) return st;
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, kv_len, block_mask,
+                  stream);
 }
 
 int fa_split_count(int N, int split_len) {
@@ -196,10 +239,15 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   return fa::bwd_workspace_bytes(B, H, N, d);
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const float* o, const void* dout,
-           const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
-           float scale, int causal, int dtype, const int32_t* kv_len, void* workspace,
-           size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int bwd_impl(const void* q, const void* k, const void* v, const float* o, const void* dout,
+             const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+             float scale, int causal, int dtype, const int32_t* kv_len,
+             const uint8_t* block_mask, void* workspace, size_t workspace_bytes,
+             void* stream) {
   clear_error();
   int st = check_common(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
@@ -218,11 +266,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const float* o, const vo
   const size_t lse_bytes = (size_t)B * H * N * 4;
   const Span ins[] = {{q, in_bytes, "q"},       {k, in_bytes, "k"},         {v, in_bytes, "v"},
                       {o, f_bytes, "o"},        {dout, in_bytes, "dout"},   {lse, lse_bytes, "lse"},
-                      {kv_len, kv_len ? (size_t)B * 4 : 0, "kv_len"}};
+                      {kv_len, kv_len ? (size_t)B * 4 : 0, "kv_len"},
+                      {block_mask, block_mask ? sparse_mask_bytes(N) : 0, "block_mask"}};
   const Span outs[] = {{dq, f_bytes, "dq"}, {dk, f_bytes, "dk"}, {dv, f_bytes, "dv"},
                        {workspace, need, "workspace"}};
   for (const Span& s : ins) {
-    const size_t al = (s.p == kv_len || s.p == lse) ? 4 : 16;
+    const size_t al = (s.p == kv_len || s.p == lse) ? 4 : s.p == block_mask ? 1 : 16;
     if (s.bytes && !aligned(s.p, al)) return fail(FA_EINVAL, "%s is not %zu-byte aligned", s.name, al);
   }
   for (const Span& s : outs)
@@ -238,9 +287,36 @@ int fa_bwd(const void* q, const void* k, const void* v, const float* o, const vo
 
   fa::BwdArgs a{q,  k,  v,  o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal ? 1 : 0,
                 dtype, kv_len, static_cast<float*>(workspace)};
+  a.block_mask = block_mask;
   hipError_t e = fa::launch_bwd(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_EHIP, "backward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd(const void* q, const void* k, const void* v, const float* o, const void* dout,
+           const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+           float scale, int causal, int dtype, const int32_t* kv_len, void* workspace,
+           size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, kv_len,
+                  nullptr, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_sparse(const void* q, const void* k, const void* v, const float* o,
+                  const void* dout, const float* lse, float* dq, float* dk, float* dv, int B,
+                  int H, int N, int d, float scale, int causal, int dtype,
+                  const int32_t* kv_len, const uint8_t* block_mask, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  clear_error();
+  int st = check_common(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  st = check_sparse(N, dtype, block_mask);
+  if (st != FA_OK) return st;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, kv_len,
+                  block_mask, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

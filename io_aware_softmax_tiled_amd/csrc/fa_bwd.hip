@@ -83,13 +83,19 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
 constexpr int kBK = 128;  // keys per workgroup
 constexpr int kBQ = 64;   // queries per tile (two 32-query halves)
 
-template <typename T, int D>
+// kSparse: bmask is the n_sb x n_sb byte matrix over 128-query x 128-key blocks (this
+// workgroup's 128 keys are one key block); query tiles in disabled blocks are skipped.
+constexpr int kSparseBlock = 128;
+constexpr int kSparseMaxBlocks = 8192;  // blocks per row/column of the mask (N <= 2^20)
+
+template <typename T, int D, bool kSparse>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ delta, float* __restrict__ dK,
     float* __restrict__ dV, int BH, int H, int N, float scale, float sl2, int causal,
-    const int* __restrict__ kv_len, int n_kblk, int heads_per_xcd) {
+    const int* __restrict__ kv_len, int n_kblk, int heads_per_xcd,
+    const uint8_t* __restrict__ bmask, int n_sb) {
   constexpr int kKC = D / 16;
   constexpr int kDB = D / 32;
   constexpr int kCPR = D / 8;                        // 16-byte chunks per row
@@ -101,6 +107,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t Ob1[kTile];
   __shared__ __attribute__((aligned(16))) float St0[2 * kBQ];  // LSE*log2(e), then D
   __shared__ __attribute__((aligned(16))) float St1[2 * kBQ];
+  __shared__ uint16_t tlist[kSparse ? 2 * kSparseMaxBlocks : 1];  // enabled query tiles
+  __shared__ int tlist_len;
 
   const WgPos pos = wg_position(heads_per_xcd, blockIdx.x);
   const int kblk = pos.blk;  // key block 0 has the most query tiles under a causal mask
@@ -135,6 +143,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
   const int nq = (N + kBQ - 1) / kBQ;
   const int i0 = causal ? k0 / kBQ : 0;
+  // the query tiles this workgroup visits: i0 .. nq-1, or (sparse) those of them in
+  // query blocks enabled for this key block, listed by wave 0
+  int nt = max(nq - i0, 0);
+  if constexpr (kSparse) {
+    if (wave == 0) {
+      int count = 0;
+      for (int base = i0; base < nq; base += 64) {
+        const int it = base + lane;
+        const bool on = it < nq && bmask[(size_t)(it * kBQ / kSparseBlock) * n_sb + kblk] != 0;
+        const uint64_t m = __ballot(on);
+        const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (on) tlist[count + before] = (uint16_t)it;
+        count += __popcll(m);
+      }
+      if (lane == 0) tlist_len = count;
+    }
+    __syncthreads();
+    nt = tlist_len;
+  }
+  auto tile_at = [&](int s) {
+    if constexpr (kSparse) return __builtin_amdgcn_readfirstlane((int)tlist[s]);
+    else return i0 + s;
+  };
 
   // staging of query tile `it` through registers (coalesced 16-byte loads)
   u32x4 qs[kSC], os[kSC];
@@ -159,7 +191,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     }
     if (tid < kBQ) {
       const size_t r = (size_t)bh * N + min(q0 + tid, N - 1);
-      s_lse = LSE[r] * kLog2e;
+      // a row that sees no key (LSE = -inf, block-sparse) must give P = 0: +inf here
+      const float l = LSE[r];
+      s_lse = l == -INFINITY ? INFINITY : l * kLog2e;
       s_dlt = delta[r];
     }
   };
@@ -177,7 +211,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     }
   };
 
-  if (i0 < nq) load_tile(i0);
+  if (nt > 0) load_tile(tile_at(0));
 
   // this lane's key row of K and V as B operands (fp16): [key][16c + 8hh + 0..7]
   u32x4 kf[kKC], vf[kKC];
@@ -213,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       toff[r][db] = tile_off<D>(8 * hh + (gi >> 2) + 4 * r, db * 4 + 2 * (g & 1) + ((gi & 3) >> 1)) +
                     8 * (gi & 1);
 
-  if (i0 < nq) store_tile((FA_LDS uint8_t*)Qb0, (FA_LDS uint8_t*)Ob0, (FA_LDS float*)St0);
+  if (nt > 0) store_tile((FA_LDS uint8_t*)Qb0, (FA_LDS uint8_t*)Ob0, (FA_LDS float*)St0);
 
   // S = Q K^T and dP = dO V^T for the 32 queries of half `hf`:
   // lane (key, hh), register r <-> query q0 + 32*hf + 16*(r/8) + 8*hh + r%8
@@ -309,12 +343,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // three regions that keep the matrix cores busy while the vector units form P and dS:
   //   products of half 0 | products of half 1 with P, dS of half 0 |
   //   dV, dK products of half 0 with P, dS of half 1 | dV, dK products of half 1.
-  auto step = [&](int it, const FA_LDS uint8_t* Qc, const FA_LDS uint8_t* Oc,
+  auto step = [&](int s, const FA_LDS uint8_t* Qc, const FA_LDS uint8_t* Oc,
                   const FA_LDS float* Stc, FA_LDS uint8_t* Qn, FA_LDS uint8_t* On,
                   FA_LDS float* Stn) {
-    barrier_lds();  // tile `it` visible; the other buffers are free
-    load_tile(min(it + 1, nq - 1));  // unconditional: same loads in flight on every path
-    const int q0 = it * kBQ;
+    barrier_lds();  // tile s visible; the other buffers are free
+    load_tile(tile_at(min(s + 1, nt - 1)));  // unconditional: same loads on every path
+    const int q0 = tile_at(s) * kBQ;
     // a tile entirely above this wave's keys' diagonal (or a wave whose keys are all
     // padded) is skipped; otherwise both halves run, and a half hidden from every key is
     // masked to P = 0 like any other hidden entry (one code path: no accumulator copies)
@@ -357,11 +391,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     store_tile(Qn, On, Stn);  // tile it+1 (clamped) into the free buffers
   };
 
-  for (int it = i0; it < nq; it += 2) {
-    step(it, (const FA_LDS uint8_t*)Qb0, (const FA_LDS uint8_t*)Ob0, (const FA_LDS float*)St0,
+  for (int s = 0; s < nt; s += 2) {
+    step(s, (const FA_LDS uint8_t*)Qb0, (const FA_LDS uint8_t*)Ob0, (const FA_LDS float*)St0,
          (FA_LDS uint8_t*)Qb1, (FA_LDS uint8_t*)Ob1, (FA_LDS float*)St1);
-    if (it + 1 < nq)
-      step(it + 1, (const FA_LDS uint8_t*)Qb1, (const FA_LDS uint8_t*)Ob1,
+    if (s + 1 < nt)
+      step(s + 1, (const FA_LDS uint8_t*)Qb1, (const FA_LDS uint8_t*)Ob1,
            (const FA_LDS float*)St1, (FA_LDS uint8_t*)Qb0, (FA_LDS uint8_t*)Ob0,
            (FA_LDS float*)St0);
   }
@@ -391,13 +425,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 constexpr int kBM = 128;  // queries per workgroup
 constexpr int kBN = 64;   // keys per tile
 
-template <typename T, int D>
+// kSparse: this workgroup's 128 queries are one query block of bmask; key tiles in
+// disabled key blocks are skipped.
+template <typename T, int D, bool kSparse>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ delta, float* __restrict__ dQ,
     int BH, int H, int N, float scale, float sl2, int causal,
-    const int* __restrict__ kv_len, int n_mblk, int heads_per_xcd) {
+    const int* __restrict__ kv_len, int n_mblk, int heads_per_xcd,
+    const uint8_t* __restrict__ bmask, int n_sb) {
   constexpr int kKC = D / 16;
   constexpr int kDB = D / 32;
   constexpr int kCPR = D / 8;
@@ -407,6 +444,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t Kb1[kTile];
   __shared__ __attribute__((aligned(1024))) uint8_t Vb0[kTile];
   __shared__ __attribute__((aligned(1024))) uint8_t Vb1[kTile];
+  __shared__ uint16_t tlist[kSparse ? 2 * kSparseMaxBlocks : 1];  // enabled key tiles
+  __shared__ int tlist_len;
 
   const WgPos pos = wg_position(heads_per_xcd, blockIdx.x);
   if (pos.bh >= BH) return;
@@ -418,11 +457,34 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   if (kv_len != nullptr) kv_lim = min(N, max(1, kv_len[b]));
   const int m0 = mblk * kBM;
   const int kend = causal ? min(kv_lim, m0 + kBM) : kv_lim;
-  const int ntiles = (kend + kBN - 1) / kBN;
+  int ntiles = (kend + kBN - 1) / kBN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  // the key tiles this workgroup visits: 0 .. ntiles-1, or (sparse) those of them in
+  // key blocks enabled for this query block, listed by wave 0
+  if constexpr (kSparse) {
+    if (wave == 0) {
+      int count = 0;
+      for (int base = 0; base < ntiles; base += 64) {
+        const int t = base + lane;
+        const bool on = t < ntiles && bmask[(size_t)mblk * n_sb + t * kBN / kSparseBlock] != 0;
+        const uint64_t m = __ballot(on);
+        const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (on) tlist[count + before] = (uint16_t)t;
+        count += __popcll(m);
+      }
+      if (lane == 0) tlist_len = count;
+    }
+    __syncthreads();
+    ntiles = tlist_len;
+  }
+  auto tile_key = [&](int t) {
+    if constexpr (kSparse) return __builtin_amdgcn_readfirstlane((int)tlist[t]) * kBN;
+    else return t * kBN;
+  };
   const int qi = lane & 31, hh = lane >> 5;
   const int g = lane >> 4, gi = lane & 15;
   const int wq0 = m0 + wave * 32;
@@ -437,7 +499,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     ld_off[j] = (uint32_t)((ci / kCPR) * D + (ci % kCPR) * 8) * 2;
   }
   auto load_tile = [&](int t) {
-    const int n0 = t * kBN;
+    const int n0 = tile_key(t);
     const uint32_t bytes = (uint32_t)(N - n0) * D * 2;
     const auto rk = buffer_rsrc(K + head + (size_t)n0 * D, bytes);
     const auto rv = buffer_rsrc(V + head + (size_t)n0 * D, bytes);
@@ -467,7 +529,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     qf[c] = to_f16x8<T>(*reinterpret_cast<const u32x4*>(Q + off));
     of[c] = to_f16x8<T>(*reinterpret_cast<const u32x4*>(dO + off));
   }
-  const float lse2 = LSE[(size_t)bh * N + qrow_c] * kLog2e;
+  // a row that sees no key (LSE = -inf, block-sparse) must give P = 0: +inf here
+  const float lse_row = LSE[(size_t)bh * N + qrow_c];
+  const float lse2 = lse_row == -INFINITY ? INFINITY : lse_row * kLog2e;
   const float dlt = delta[(size_t)bh * N + qrow_c];
   f32x16 dqacc[kDB];
 #pragma unroll
@@ -482,7 +546,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                   FA_LDS uint8_t* Vn) {
     barrier_lds();  // tile t visible; the other buffers are free
     load_tile(min(t + 1, ntiles - 1));  // unconditional: same loads in flight on every path
-    const int n0 = t * kBN;
+    const int n0 = tile_key(t);
     const bool need_mask = (n0 + kBN > kv_lim) || (causal && n0 + kBN - 1 > wq0);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -579,22 +643,31 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   const auto* k16 = static_cast<const uint16_t*>(a.k);
   const auto* v16 = static_cast<const uint16_t*>(a.v);
   const auto* dO16 = static_cast<const uint16_t*>(a.dout);
-#define FA_BWD_LAUNCH(TAG, DIM)                                                              \
+  const int n_sb = (a.N + kSparseBlock - 1) / kSparseBlock;
+#define FA_BWD_LAUNCH2(TAG, DIM, SP)                                                         \
   do {                                                                                       \
     hipLaunchKernelGGL((bwd_pre_kernel<TAG, DIM>), dim3(pre_blocks), dim3(kThreads), 0,      \
                        stream, dO16, a.o, a.delta, rows);                                    \
-    hipLaunchKernelGGL((bwd_dkdv_kernel<TAG, DIM>), dim3(8 * hpx * n_kblk), dim3(kThreads),  \
-                       0, stream, q16, k16, v16, dO16, a.lse, a.delta, a.dk, a.dv, BH, a.H,  \
-                       a.N, a.scale, sl2, a.causal, a.kv_len, n_kblk, hpx);                  \
-    hipLaunchKernelGGL((bwd_dq_kernel<TAG, DIM>), dim3(8 * hpx * n_mblk), dim3(kThreads), 0, \
-                       stream, q16, k16, v16, dO16, a.lse, a.delta, a.dq, BH, a.H, a.N,      \
-                       a.scale, sl2, a.causal, a.kv_len, n_mblk, hpx);                       \
+    hipLaunchKernelGGL((bwd_dkdv_kernel<TAG, DIM, SP>), dim3(8 * hpx * n_kblk),              \
+                       dim3(kThreads), 0, stream, q16, k16, v16, dO16, a.lse, a.delta, a.dk, \
+                       a.dv, BH, a.H, a.N, a.scale, sl2, a.causal, a.kv_len, n_kblk, hpx,    \
+                       a.block_mask, n_sb);                                                  \
+    hipLaunchKernelGGL((bwd_dq_kernel<TAG, DIM, SP>), dim3(8 * hpx * n_mblk),                \
+                       dim3(kThreads), 0, stream, q16, k16, v16, dO16, a.lse, a.delta, a.dq, \
+                       BH, a.H, a.N, a.scale, sl2, a.causal, a.kv_len, n_mblk, hpx,          \
+                       a.block_mask, n_sb);                                                  \
+  } while (0)
+#define FA_BWD_LAUNCH(TAG, DIM)                             \
+  do {                                                      \
+    if (a.block_mask != nullptr) FA_BWD_LAUNCH2(TAG, DIM, true); \
+    else FA_BWD_LAUNCH2(TAG, DIM, false);                   \
   } while (0)
   if (a.dtype == kDtypeBF16) {
     if (a.d == 64) FA_BWD_LAUNCH(BF16, 64); else FA_BWD_LAUNCH(BF16, 128);
   } else {
     if (a.d == 64) FA_BWD_LAUNCH(F16, 64); else FA_BWD_LAUNCH(F16, 128);
   }
+#undef FA_BWD_LAUNCH2
 #undef FA_BWD_LAUNCH
   return hipGetLastError();
 }

@@ -59,17 +59,29 @@ constexpr int kThreads = 256;
 // loaded into LDS serves 256 query rows, halving the tile traffic per FLOP; 4 waves
 // keep enough workgroups for small problems.
 //
-// kPartial: split-KV. Workgroup index = split * per_split + (position as above); split p
+// kMode 1, split-KV: workgroup index = split * per_split + (position as above); split p
 // covers keys [p*split_len, (p+1)*split_len) and writes its normalised partial output
-// and LSE at O + p*o_stride, LSE + p*lse_stride. A row that sees no key of its split
-// gets O = 0 and LSE = -inf.
-template <typename T, int D, int W, bool kPartial>
+// and LSE at O + p*o_stride, LSE + p*lse_stride.
+// kMode 2, block-sparse: bmask is an n_sb x n_sb byte matrix over 128-row query blocks
+// and 128-key blocks; key blocks whose entry is 0 for the query block are hidden. Each
+// workgroup first lists the key blocks enabled for any of its query blocks (the LDS
+// list below) and streams only those tiles; a wave whose own query block leaves a
+// listed key block disabled masks it.
+// In both modes a row that sees no key gets O = 0 and LSE = -inf.
+constexpr int kSparseBlock = 128;
+constexpr int kSparseMaxBlocks = 8192;  // key blocks per row of the mask (N <= 2^20)
+
+template <typename T, int D, int W, int kMode>
 __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
     int BH, int H, int N, float scale, float sl2, int causal,
     const int* __restrict__ kv_len, int n_mblk, int heads_per_xcd, int split_len,
-    int per_split, size_t o_stride, size_t lse_stride) {
+    int per_split, size_t o_stride, size_t lse_stride, const uint8_t* __restrict__ bmask,
+    int n_sb) {
+  constexpr bool kPartial = kMode == 1;
+  constexpr bool kSparse = kMode == 2;
+  constexpr bool kGuard = kMode != 0;  // rows may see no key at all
   constexpr int kTileBytes = kBN * D * 2;              // one K or V tile
   constexpr int kKC = D / 16;                          // 16-wide k-steps over head_dim
   constexpr int kDB = D / 32;                          // 32-row blocks of O^T
@@ -85,6 +97,10 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   __shared__ __attribute__((aligned(1024))) uint8_t Vb0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t Vb1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t Vb2[kTileBytes];
+  // block-sparse: enabled key blocks of this workgroup, each entry kb | (enabled for the
+  // first query block) << 14 | (enabled for the second) << 15, then a sentinel 0
+  __shared__ uint16_t blist[kSparse ? kSparseMaxBlocks + 1 : 1];
+  __shared__ int blist_len;
 
   int split = 0, wid = blockIdx.x;
   if constexpr (kPartial) {
@@ -113,7 +129,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   const int kv_hi = kPartial ? min(kv_lim, kbeg + split_len) : kv_lim;
   const int kend = causal ? min(kv_hi, m0 + kBMw) : kv_hi;
   // >= 1 without a split (key 0 is always visible); a split may hold no visible key
-  const int ntiles = kend > kbeg ? (kend - kbeg + kBN - 1) / kBN : 0;
+  int ntiles = kend > kbeg ? (kend - kbeg + kBN - 1) / kBN : 0;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -124,8 +140,40 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   const int qrow = wq0 + qi;
   const int qrow_c = min(qrow, N - 1);
 
-  if constexpr (kPartial) {
-    if (ntiles == 0) {  // no key of the split is visible to this block: empty partials
+  // block-sparse: which of the workgroup's (one or two) query blocks this wave is in
+  const int qb_lo = m0 / kSparseBlock;
+  const int wave_flag = (wq0 / kSparseBlock == qb_lo) ? (1 << 14) : (1 << 15);
+  if constexpr (kSparse) {
+    // wave 0 compacts the enabled key blocks below the workgroup's last visible key
+    if (wave == 0) {
+      const int qb_hi = (m0 + kBMw - 1) / kSparseBlock;
+      const int nkb = (kend + kSparseBlock - 1) / kSparseBlock;
+      int count = 0;
+      for (int base = 0; base < nkb; base += 64) {
+        const int kb = base + lane;
+        int entry = 0;
+        if (kb < nkb) {
+          const bool f0 = bmask[(size_t)qb_lo * n_sb + kb] != 0;
+          const bool f1 = qb_hi != qb_lo && qb_hi < n_sb && bmask[(size_t)qb_hi * n_sb + kb] != 0;
+          entry = kb | (f0 ? 1 << 14 : 0) | (f1 ? 1 << 15 : 0);
+        }
+        const uint64_t on = __ballot(entry >> 14);
+        const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(on >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)on, 0));
+        if (entry >> 14) blist[count + before] = (uint16_t)entry;
+        count += __popcll(on);
+      }
+      if (lane == 0) {
+        blist[count] = 0;  // sentinel: a block enabled for nobody
+        blist_len = count;
+      }
+    }
+    __syncthreads();
+    ntiles = 2 * blist_len;
+  }
+
+  if constexpr (kGuard) {
+    if (ntiles == 0) {  // no key is visible to this block: empty rows
       if (qrow < N) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         float* orow = O + head + (size_t)qrow * D;
@@ -147,9 +195,17 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
     const int ci = tid + kThr * j;
     ld_off[j] = (uint32_t)((ci / kCPR) * D + (ci % kCPR) * 8) * 2;
   }
+  // first key of tile t (64 keys) and of sub-block sb (32 keys)
+  auto tile_key = [&](int t) {
+    if constexpr (kSparse)
+      return __builtin_amdgcn_readfirstlane((blist[t >> 1] & 0x1fff) * kSparseBlock + (t & 1) * kBN);
+    else
+      return kbeg + t * kBN;
+  };
   auto load_kv = [&](int t) {
-    const int n0 = kbeg + t * kBN;
-    const uint32_t bytes = (uint32_t)(N - n0) * D * 2;
+    const int n0 = tile_key(t);
+    // (a sparse list may name a tile past the end of the sequence: zero bytes)
+    const uint32_t bytes = (uint32_t)max(N - n0, 0) * D * 2;
     const auto rk = buffer_rsrc(k + (size_t)n0 * D, bytes);
     const auto rv = buffer_rsrc(v + (size_t)n0 * D, bytes);
 #pragma unroll
@@ -242,9 +298,10 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   };
   // P = exp2(s*scale*log2e - m_ref*scale*log2e), rounded to fp16, and its row sum
   auto expo = [&](const f32x16& s, uint32_t (&pk)[8]) {
-    // (a row that has seen no visible key yet -- possible only in a split -- keeps
+    // (a row that has seen no visible key yet -- possible in a split or a sparse
+    // pattern -- keeps
     // m_ref = -inf; its scores are all -inf and must give P = 0, not NaN)
-    const float nms = (kPartial && m_ref == -INFINITY) ? 0.f : -m_ref * sl2;
+    const float nms = (kGuard && m_ref == -INFINITY) ? 0.f : -m_ref * sl2;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float p0 = exp2_fast(fmaf(s[2 * i], sl2, nms));
@@ -294,9 +351,15 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   // sixteen.
   const int last_vis = (causal ? min(kv_hi - 1, qrow) : kv_hi - 1) - 8 * hh;
   auto mask = [&](f32x16& s, int sb) {
-    const int n0 = kbeg + 32 * sb;
-    if ((n0 + 32 > kv_hi) || (causal && n0 + 31 > wq0)) {
-      const int lim = last_vis - n0;
+    int n0 = kbeg + 32 * sb;
+    bool off = false;  // block-sparse: the whole sub-block is disabled for this wave
+    if constexpr (kSparse) {
+      const int e = __builtin_amdgcn_readfirstlane(blist[sb >> 2]);
+      n0 = (e & 0x1fff) * kSparseBlock + (sb & 3) * 32;
+      off = (e & wave_flag) == 0;
+    }
+    if (off || (n0 + 32 > kv_hi) || (causal && n0 + 31 > wq0)) {
+      const int lim = off ? -1 : last_vis - n0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = (16 * (r >> 3) + (r & 7) > lim) ? -INFINITY : s[r];
     }
@@ -388,8 +451,8 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   // epilogue: O = O_acc / l, LSE = scale*m_ref + ln(l)
   const float ltot = sum_halves(lsum);
   if (qrow < N) {
-    // a row with no visible key in its split (ltot = 0) gets O = 0, LSE = -inf
-    const bool empty = kPartial && !(ltot > 0.f);
+    // a row with no visible key (split or sparse pattern: ltot = 0) gets O = 0, LSE = -inf
+    const bool empty = kGuard && !(ltot > 0.f);
     const float inv = empty ? 0.f : 1.0f / ltot;
     float* orow = O + head + (size_t)qrow * D;
 #pragma unroll
@@ -587,23 +650,26 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   const float sl2 = a.scale * kLog2e;
   const int BH = a.B * a.H;
   const bool partial = a.split_len > 0;
+  const bool sparse = a.block_mask != nullptr;
   const int n_splits = partial ? (a.N + a.split_len - 1) / a.split_len : 1;
   const size_t o_stride = (size_t)BH * a.N * a.d, lse_stride = (size_t)BH * a.N;
-#define FA_LAUNCH16W(TAG, DIM, WV, PART)                                                   \
-  hipLaunchKernelGGL((fwd_kernel_16<TAG, DIM, WV, PART>), dim3(g.blocks * n_splits),        \
+  const int n_sb = (a.N + kSparseBlock - 1) / kSparseBlock;
+#define FA_LAUNCH16W(TAG, DIM, WV, MODE)                                                   \
+  hipLaunchKernelGGL((fwd_kernel_16<TAG, DIM, WV, MODE>), dim3(g.blocks * n_splits),        \
                      dim3(WV * 64), 0, stream, q16, k16, v16, a.o, a.lse, BH, a.H, a.N,     \
                      a.scale, sl2, a.causal, a.kv_len, g.n_mblk, g.heads_per_xcd,           \
-                     a.split_len, g.blocks, o_stride, lse_stride)
+                     a.split_len, g.blocks, o_stride, lse_stride, a.block_mask, n_sb)
   // head_dim 128 always runs 8 waves (its LDS use allows one workgroup per CU)
-#define FA_LAUNCH16(TAG, DIM, PART)                                 \
+#define FA_LAUNCH16(TAG, DIM, MODE)                                 \
   do {                                                              \
-    if (DIM == 128 || waves == 8) FA_LAUNCH16W(TAG, DIM, 8, PART);  \
-    else FA_LAUNCH16W(TAG, 64, 4, PART);                            \
+    if (DIM == 128 || waves == 8) FA_LAUNCH16W(TAG, DIM, 8, MODE);  \
+    else FA_LAUNCH16W(TAG, 64, 4, MODE);                            \
   } while (0)
 #define FA_LAUNCH16P(TAG, DIM)                       \
   do {                                               \
-    if (partial) FA_LAUNCH16(TAG, DIM, true);        \
-    else FA_LAUNCH16(TAG, DIM, false);               \
+    if (partial) FA_LAUNCH16(TAG, DIM, 1);           \
+    else if (sparse) FA_LAUNCH16(TAG, DIM, 2);       \
+    else FA_LAUNCH16(TAG, DIM, 0);                   \
   } while (0)
 #define FA_LAUNCH32(DIM)                                                                  \
   hipLaunchKernelGGL((fwd_kernel_f32<DIM>), dim3(g.blocks), dim3(kThreads), 0, stream,    \
@@ -615,7 +681,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   } else if (a.dtype == kDtypeF16) {
     if (a.d == 64) FA_LAUNCH16P(F16, 64); else FA_LAUNCH16P(F16, 128);
   } else {
-    if (partial) return hipErrorNotSupported;  // rejected by the API layer
+    if (partial || sparse) return hipErrorNotSupported;  // rejected by the API layer
     if (a.d == 64) FA_LAUNCH32(64); else FA_LAUNCH32(128);
   }
 #undef FA_LAUNCH16P

@@ -24,6 +24,9 @@ struct FwdArgs {
   // split-KV: keys per split (a multiple of 64), 0 for none. With a split, o and lse
   // point at [n_splits, B, H, N, d] and [n_splits, B, H, N] partial outputs.
   int split_len = 0;
+  // block-sparse: ceil(N/128) x ceil(N/128) bytes, nonzero = (query block, key block)
+  // evaluated; nullptr for dense attention
+  const uint8_t* block_mask = nullptr;
 };
 
 struct FwdGrid {
@@ -51,6 +54,7 @@ struct BwdArgs {
   int dtype;
   const int* kv_len;
   float* delta;  // workspace: D_i = rowsum(dO * O), [B,H,N]
+  const uint8_t* block_mask = nullptr;  // block-sparse mask as in FwdArgs, or nullptr
 };
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d);

@@ -30,9 +30,10 @@ def lib():
 
 
 def test_header_declares_the_api():
-    assert declared_symbols() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd",
-                                  "fa_fwd_partial", "fa_last_error", "fa_merge",
-                                  "fa_split_count", "fa_status_str", "fa_version"]
+    assert declared_symbols() == ["fa_bwd", "fa_bwd_sparse", "fa_bwd_workspace_size",
+                                  "fa_fwd", "fa_fwd_partial", "fa_fwd_sparse",
+                                  "fa_last_error", "fa_merge", "fa_split_count",
+                                  "fa_status_str", "fa_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -200,3 +201,39 @@ def test_merge_rejects_before_launch(lib, kw, code):
 
 def test_merge_empty_is_noop(lib):
     assert _merge(lib, N=0) == FA_OK
+
+
+# ---- block-sparse --------------------------------------------------------------------
+
+def _sfwd(lib, mask=P + 0x800000, N=256, dtype=1, **kw):
+    args = dict(q=P, k=P + 0x100000, v=P + 0x200000, o=P + 0x300000, lse=P + 0x700000)
+    args.update(kw)
+    return lib.fa_fwd_sparse(args["q"], args["k"], args["v"], args["o"], args["lse"], 1, 1, N,
+                             64, 0.125, 0, dtype, None, mask, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=None), FA_EINVAL),
+    (dict(dtype=0), FA_EUNSUPPORTED),
+    (dict(N=(1 << 20) + 1), FA_EINVAL),
+    (dict(mask=P + 0x300000 + 8), FA_EINVAL),   # o overlaps the mask
+    (dict(q=None), FA_EINVAL),
+])
+def test_sparse_fwd_rejects_before_launch(lib, kw, code):
+    assert _sfwd(lib, **kw) == code
+    assert fa.fa_last_error() != ""
+
+
+def test_sparse_bwd_rejects_before_launch(lib):
+    args = [P, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x400000, P + 0x500000,
+            P + 0x600000, P + 0x700000, P + 0x800000, 1, 1, 256, 64, 0.125, 0, 1, None]
+    ws = lib.fa_bwd_workspace_size(1, 1, 256, 64)
+    assert lib.fa_bwd_sparse(*args, None, P + 0xa00000, ws, None) == FA_EINVAL
+    assert lib.fa_bwd_sparse(*args[:15], 0, None, P + 0x900000, P + 0xa00000, ws,
+                             None) == FA_EUNSUPPORTED
+    assert lib.fa_bwd_sparse(*args, P + 0x900000, None, 0, None) == FA_EWORKSPACE
+    assert lib.fa_bwd_sparse(*args, P + 0x600000 + 16, P + 0xa00000, ws, None) == FA_EINVAL
+
+
+def test_sparse_empty_is_noop(lib):
+    assert _sfwd(lib, N=0, mask=None) == FA_OK
