@@ -11,7 +11,8 @@ Prints ONE JSON line with the throughput, the roofline of the dominant call
 (measured with HIP events on the stream the kernels run on) and the CPU oracle's
 throughput on a bounded sample of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--gpus 1] [--sweep] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--sweep] [--split-kv] [--sparse]
+                  [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -125,6 +126,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sweep", action="store_true",
                     help="also print one line per sequence length (supplementary)")
+    ap.add_argument("--split-kv", action="store_true",
+                    help="also print split-KV lines: partial forward + merge against the "
+                         "unsplit forward (supplementary)")
+    ap.add_argument("--sparse", action="store_true",
+                    help="also print block-sparse lines: forward and backward time against the "
+                         "fraction of 128x128 blocks evaluated (supplementary)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy a MIB-MiB buffer once (a plain copy kernel of known size, "
@@ -206,6 +213,10 @@ def main():
 
     if args.sweep:
         sweep(fa, torch, workloads)
+    if args.split_kv:
+        split_kv(fa, torch, workloads)
+    if args.sparse:
+        sparse(fa, torch, workloads)
 
 
 def sweep(fa, torch, workloads):
@@ -221,6 +232,98 @@ def sweep(fa, torch, workloads):
                     "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
                     "fwd_tflops": round(w.fwd_flops() / fwd_ms / 1e9, 2),
                     "bwd_tflops": round(w.bwd_flops() / bwd_ms / 1e9, 2)}), flush=True)
+
+
+def _time(torch, fn, iters=20, warmup=3):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def split_kv(fa, torch, workloads):
+    """Supplementary lines: fa_fwd_partial + fa_merge against fa_fwd on shapes with few
+    query blocks per CU (where splitting the key axis adds workgroups) and on the
+    benchmarked shape. Outputs are preallocated; the merge's HBM rate is its
+    algorithmic bytes (n_splits*(d+1) floats read, d+1 written per row) over its time."""
+    shapes = [(1, 4, 8192, 128, False), (1, 8, 16384, 64, False), (2, 16, 4096, 128, True)]
+    for B, H, N, d, causal in shapes:
+        w, inp = workloads.custom(B, H, N, d, "bf16", causal, seed=0, with_dout=False)
+        dev = {n: inp[n].cuda() for n in ("q", "k", "v")}
+        o = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        t_full = _time(torch, lambda: fa.fa_fwd(dev["q"], dev["k"], dev["v"], causal=causal,
+                                                scale=w.scale, out=o, lse=lse))
+        for split_len in (N // 8, N // 4, N // 2):
+            P = fa.fa_split_count(N, split_len)
+            o_p = torch.empty((P, B, H, N, d), dtype=torch.float32, device="cuda")
+            l_p = torch.empty((P, B, H, N), dtype=torch.float32, device="cuda")
+            part = lambda: fa.fa_fwd_partial(dev["q"], dev["k"], dev["v"], split_len=split_len,
+                                             causal=causal, scale=w.scale, out=o_p, lse=l_p)
+            merge = lambda: fa.fa_merge(o_p, l_p, out=o, lse=lse)
+            t_part = _time(torch, part)
+            t_merge = _time(torch, merge)
+            merge_bytes = 4.0 * B * H * N * (P * (d + 1) + (d + 1))
+            print(json.dumps({
+                "split_kv": True, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                "split_len": split_len, "n_splits": P,
+                "unsplit_fwd_ms": round(t_full, 4), "partial_ms": round(t_part, 4),
+                "merge_ms": round(t_merge, 4),
+                "split_total_ms": round(t_part + t_merge, 4),
+                "unsplit_tflops": round(w.fwd_flops() / t_full / 1e9, 2),
+                "split_tflops": round(w.fwd_flops() / (t_part + t_merge) / 1e9, 2),
+                "merge_hbm_gbs": round(merge_bytes / t_merge / 1e6, 1),
+                "merge_hbm_frac": round(merge_bytes / t_merge / 1e6 / PEAK_HBM_GBS, 4)}),
+                flush=True)
+            del o_p, l_p
+
+
+def sparse(fa, torch, workloads):
+    """Supplementary lines: block-sparse forward/backward time against the fraction of
+    evaluated 128x128 blocks (random, diagonal blocks always on), next to the dense
+    kernels on the same inputs. FLOPs are counted over the evaluated blocks only."""
+    import numpy as np
+    blk = fa.FA_SPARSE_BLOCK
+    for B, H, N, d, causal in [(2, 16, 4096, 128, True), (1, 16, 8192, 64, False)]:
+        w, inp = workloads.custom(B, H, N, d, "bf16", causal, seed=0)
+        dev = {n: inp[n].cuda() for n in ("q", "k", "v", "dout")}
+        nb = N // blk
+        ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8,
+                         device="cuda")
+        o, lse = fa.fa_fwd(dev["q"], dev["k"], dev["v"], causal=causal, scale=w.scale)
+        t_fd = _time(torch, lambda: fa.fa_fwd(dev["q"], dev["k"], dev["v"], causal=causal,
+                                              scale=w.scale, out=o, lse=lse))
+        t_bd = _time(torch, lambda: fa.fa_bwd(dev["q"], dev["k"], dev["v"], o, dev["dout"], lse,
+                                              causal=causal, scale=w.scale, workspace=ws))
+        full = np.tril(np.ones((nb, nb))) if causal else np.ones((nb, nb))
+        for density in (1.0, 0.5, 0.25, 0.125):
+            rng = np.random.default_rng(1)
+            m = ((rng.random((nb, nb)) < density) * full).astype(np.uint8)
+            np.fill_diagonal(m, 1)
+            bm = torch.from_numpy(m).cuda()
+            frac = float(m.sum() / full.sum())
+            os_, ls_ = fa.fa_fwd_sparse(dev["q"], dev["k"], dev["v"], bm, causal=causal,
+                                        scale=w.scale)
+            t_f = _time(torch, lambda: fa.fa_fwd_sparse(dev["q"], dev["k"], dev["v"], bm,
+                                                        causal=causal, scale=w.scale,
+                                                        out=os_, lse=ls_))
+            t_b = _time(torch, lambda: fa.fa_bwd_sparse(dev["q"], dev["k"], dev["v"], os_,
+                                                        dev["dout"], ls_, bm, causal=causal,
+                                                        scale=w.scale, workspace=ws))
+            print(json.dumps({
+                "sparse": True, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                "block": blk, "blocks_on_frac": round(frac, 4),
+                "dense_fwd_ms": round(t_fd, 4), "dense_bwd_ms": round(t_bd, 4),
+                "sparse_fwd_ms": round(t_f, 4), "sparse_bwd_ms": round(t_b, 4),
+                "fwd_time_frac": round(t_f / t_fd, 4), "bwd_time_frac": round(t_b / t_bd, 4),
+                "sparse_fwd_tflops": round(frac * w.fwd_flops() / t_f / 1e9, 2),
+                "sparse_bwd_tflops": round(frac * w.bwd_flops() / t_b / 1e9, 2)}), flush=True)
 
 
 if __name__ == "__main__":
