@@ -167,7 +167,7 @@ FA_API int fa_merge(const float* o_part, const float* lse_part, float* o, float*
  * come from fa_fwd_sparse with the same mask).
  */
 #define FA_SPARSE_BLOCK 128
-#define FA_SPARSE_MAX_N (1 << 20)
+#define FA_SPARSE_MAX_N (1 << 18)
 
 FA_API int fa_fwd_sparse(const void* q, const void* k, const void* v, float* o, float* lse,
                   int B, int H, int N, int d, float scale, int causal, int dtype,

@@ -86,7 +86,7 @@ constexpr int kBQ = 64;   // queries per tile (two 32-query halves)
 // kSparse: bmask is the n_sb x n_sb byte matrix over 128-query x 128-key blocks (this
 // workgroup's 128 keys are one key block); query tiles in disabled blocks are skipped.
 constexpr int kSparseBlock = 128;
-constexpr int kSparseMaxBlocks = 8192;  // blocks per row/column of the mask (N <= 2^20)
+constexpr int kSparseMaxBlocks = 2048;  // blocks per row/column of the mask (N <= 2^18)
 
 template <typename T, int D, bool kSparse>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(

@@ -69,7 +69,7 @@ constexpr int kThreads = 256;
 // listed key block disabled masks it.
 // In both modes a row that sees no key gets O = 0 and LSE = -inf.
 constexpr int kSparseBlock = 128;
-constexpr int kSparseMaxBlocks = 8192;  // key blocks per row of the mask (N <= 2^20)
+constexpr int kSparseMaxBlocks = 2048;  // key blocks per row of the mask (N <= 2^18)
 
 template <typename T, int D, int W, int kMode>
 __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(

@@ -215,7 +215,7 @@ def _sfwd(lib, mask=P + 0x800000, N=256, dtype=1, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(mask=None), FA_EINVAL),
     (dict(dtype=0), FA_EUNSUPPORTED),
-    (dict(N=(1 << 20) + 1), FA_EINVAL),
+    (dict(N=(1 << 18) + 1), FA_EINVAL),
     (dict(mask=P + 0x300000 + 8), FA_EINVAL),   # o overlaps the mask
     (dict(q=None), FA_EINVAL),
 ])
