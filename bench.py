@@ -7,9 +7,9 @@ generator and resident in HBM before timing). The metric is attention TFLOP/s un
 the nominal count 4*B*H*N^2*d (halved when causal) for the forward pass plus 2.5x
 that for the backward pass, against the dense bf16 matrix-core peak.
 
-Prints ONE JSON line with the throughput, the roofline of the dominant call
-(measured with HIP events on the stream the kernels run on) and the CPU oracle's
-throughput on a bounded sample of the same workload.
+Prints ONE JSON line with the throughput, the roofline of the dominant kernel (each
+kernel of the step timed with HIP events on the stream it runs on: fa_bwd is run as its
+three stages) and the CPU oracle's throughput on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--sweep] [--split-kv] [--sparse]
                   [--no-cpu-baseline]
@@ -42,9 +42,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, launches_per_step: int = 1):
-    """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs, scaled by
-    the copy-kernel calibration, or None when absent or taken on other kernel sources."""
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` (a name prefix such as "bwd_dkdv_kernel") from the
+    committed rocprofv3 counter runs, scaled by the copy-kernel calibration, or None when
+    absent or taken on other kernel sources."""
     try:
         with open(PROFILE_COUNTERS) as f:
             rec = json.load(f)
@@ -52,10 +53,10 @@ def measured_traffic(kernel: str, launches_per_step: int = 1):
         return None
     if rec.get("source_hash") != kernel_source_hash():
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    if not k:
-        return None
-    return k.get("hbm_bytes_per_launch")
+    for name, k in rec.get("kernels", {}).items():
+        if name.startswith(kernel) and "hbm_bytes_per_launch" in k:
+            return k["hbm_bytes_per_launch"]
+    return None
 
 
 def cpu_baseline(inp, w, budget_heads=None):
@@ -85,27 +86,38 @@ def cpu_baseline(inp, w, budget_heads=None):
 
 
 def run_step(fa, dev, w, ws, events=None):
+    """fa_fwd, then fa_bwd as its three stages (the same kernels fa_bwd launches, in the
+    same order on the same stream), with events between the kernels when given."""
+    rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
     o, lse = fa.fa_fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale,
                        out=dev["o"], lse=dev["lse"])
-    if events is not None:
-        events[1].record()
-    dq, dk, dv = fa.fa_bwd(dev["q"], dev["k"], dev["v"], o, dev["dout"], lse,
-                           causal=w.causal, scale=w.scale, workspace=ws)
-    if events is not None:
-        events[2].record()
-    return dq
+    rec(1)
+    for stage in range(3):
+        fa.fa_bwd_stage(stage, dev["q"], dev["k"], dev["v"], o, dev["dout"], lse, dev["dq"],
+                        dev["dk"], dev["dv"], ws, causal=w.causal, scale=w.scale)
+        rec(2 + stage)
+    return dev["dq"]
+
+
+# kernels of one step, in launch order, and the MFMA FLOPs each performs as a multiple
+# of the nominal forward count (the forward: 2 products; dK/dV: S, dP, dV, dK; dQ: S, dP,
+# dQ; D: none -- it is bound by HBM)
+KERNELS = [("fwd_kernel_16", 1.0), ("bwd_pre_kernel", 0.0), ("bwd_dkdv_kernel", 2.0),
+           ("bwd_dq_kernel", 1.5)]
 
 
 def bench_workload(fa, torch, w, inp, steps, warmup):
     dev = {n: inp[n].cuda() for n in ("q", "k", "v", "dout")}
     dev["o"] = torch.empty(dev["q"].shape, dtype=torch.float32, device="cuda")
     dev["lse"] = torch.empty(dev["q"].shape[:3], dtype=torch.float32, device="cuda")
+    for n in ("dq", "dk", "dv"):
+        dev[n] = torch.empty(dev["q"].shape, dtype=torch.float32, device="cuda")
     ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8,
                      device="cuda")
     for _ in range(warmup):
         run_step(fa, dev, w, ws)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -114,9 +126,10 @@ def bench_workload(fa, torch, w, inp, steps, warmup):
         run_step(fa, dev, w, ws, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = [a.elapsed_time(b) for a, b, _ in evs]
-    bwd_ms = [b.elapsed_time(c) for _, b, c in evs]
-    return wall * 1e3 / steps, sum(fwd_ms) / steps, sum(bwd_ms) / steps
+    per_kernel = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j in range(4)]
+    fwd_ms = per_kernel[0]
+    bwd_ms = sum(per_kernel[1:])
+    return wall * 1e3 / steps, fwd_ms, bwd_ms, per_kernel
 
 
 def main():
@@ -161,29 +174,32 @@ def main():
         del src, dst
     w = workloads.WORKLOADS[WORKLOAD_ID]
     inp = workloads.draw(w)
-    ms_step, fwd_ms, bwd_ms = bench_workload(fa, torch, w, inp, args.steps, args.warmup)
+    ms_step, fwd_ms, bwd_ms, per_kernel = bench_workload(fa, torch, w, inp, args.steps,
+                                                          args.warmup)
 
     fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
     value = (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
     fwd_tf = fwd_f / (fwd_ms * 1e-3) / 1e12
     bwd_tf = bwd_f / (bwd_ms * 1e-3) / 1e12
-    # the dominant call of the step; its kernels: fwd = one kernel, bwd = pre + main
-    if bwd_ms >= fwd_ms:
-        dom = {"kernel": "fa_bwd (bwd_pre_kernel + bwd_dkdv_kernel + bwd_dq_kernel)", "ms": bwd_ms,
-               "flops": bwd_f, "traffic_key": "fa_bwd"}
-    else:
-        dom = {"kernel": "fwd_kernel_16", "ms": fwd_ms, "flops": fwd_f,
-               "traffic_key": "fa_fwd"}
-    achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+    kernels = {}
+    for (name, mult), ms in zip(KERNELS, per_kernel):
+        kernels[name] = {"ms": round(ms, 4)}
+        if mult:
+            kernels[name]["tflops"] = round(mult * fwd_f / (ms * 1e-3) / 1e12, 2)
+    # the dominant kernel of the step: the longest average launch, timed live with HIP
+    # events on the stream it runs on; achieved = its own MFMA FLOPs / its time
+    dom = max(range(4), key=lambda j: per_kernel[j])
+    name, mult = KERNELS[dom]
+    achieved = mult * fwd_f / (per_kernel[dom] * 1e-3) / 1e12
     roofline = {
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": measured_traffic(dom["traffic_key"]),
-        "kernel": dom["kernel"],
-        "avg_launch_ms": round(dom["ms"], 4),
+        "traffic": measured_traffic(name),
+        "kernel": name,
+        "avg_launch_ms": round(per_kernel[dom], 4),
     }
     line = {
         "metric": "attention fwd+bwd TFLOP/s (nominal 4BHN^2d/2 causal fwd + 2.5x bwd) and "
@@ -206,6 +222,7 @@ def main():
                            "pct_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2)},
                    "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 2),
                            "pct_peak": round(100 * bwd_tf / PEAK_BF16_TFLOPS, 2)}},
+        "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(inp, w),
     }
@@ -226,7 +243,7 @@ def sweep(fa, torch, workloads):
             for N in (512, 1024, 2048, 4096, 8192, 16384):
                 B, H = max(1, 16384 // N), 2048 // d
                 w, inp = workloads.custom(B, H, N, d, "bf16", causal, seed=0)
-                ms_step, fwd_ms, bwd_ms = bench_workload(fa, torch, w, inp, 10, 3)
+                ms_step, fwd_ms, bwd_ms, _ = bench_workload(fa, torch, w, inp, 10, 3)
                 print(json.dumps({
                     "sweep": True, "B": B, "H": H, "N": N, "d": d, "causal": causal,
                     "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),

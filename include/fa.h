@@ -179,6 +179,20 @@ FA_API int fa_bwd_sparse(const void* q, const void* k, const void* v, const floa
                   const int32_t* kv_len, const uint8_t* block_mask, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/*
+ * One stage of fa_bwd: stage 0 writes D = rowsum(dout * o) into the workspace, stage 1
+ * writes dk and dv (reads D), stage 2 writes dq (reads D). fa_bwd is stages 0, 1, 2 in
+ * order on one stream; stages 1 and 2 are independent of each other once stage 0 has
+ * run, so a caller may also put them on two streams, or time each kernel with events
+ * between the calls. Arguments, checks and errors are those of fa_bwd (every pointer is
+ * validated even where the stage does not touch it); stage outside 0..2 is FA_EINVAL.
+ */
+FA_API int fa_bwd_stage(int stage, const void* q, const void* k, const void* v,
+                 const float* o, const void* dout, const float* lse, float* dq, float* dk,
+                 float* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+                 const int32_t* kv_len, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
 /* Static description of a status code. */
 FA_API const char* fa_status_str(int status);
 

@@ -10,6 +10,7 @@ function here fails loudly when the library has not been built
 Functions have the C entry points' names:
     fa_fwd(q, k, v, *, causal=False, scale=None, kv_len=None) -> (o, lse)
     fa_bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, kv_len=None) -> (dq, dk, dv)
+    fa_bwd_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, workspace, *, ...) -> None
     fa_bwd_workspace_size(B, H, N, d) -> int
     fa_split_count(N, split_len) -> int
     fa_fwd_partial(q, k, v, *, split_len, causal=False, scale=None, kv_len=None)
@@ -30,7 +31,7 @@ import os
 
 import torch
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_split_count", "fa_fwd_partial",
+__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_split_count", "fa_fwd_partial",
            "fa_merge", "fa_fwd_sparse", "fa_bwd_sparse", "FA_SPARSE_BLOCK", "fa_status_str", "fa_last_error", "fa_version", "FaError", "lib_path",
            "load_library",
            "FA_F32", "FA_BF16", "FA_F16"]
@@ -69,6 +70,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32,
                            i32, vp, vp, sz, vp]
     lib.fa_bwd.restype = i32
+    lib.fa_bwd_stage.argtypes = [i32] + lib.fa_bwd.argtypes
+    lib.fa_bwd_stage.restype = i32
     lib.fa_bwd_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_split_count.argtypes = [i32, i32]
@@ -193,6 +196,23 @@ def fa_bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, kv_len=None, work
                         _stream(q.device, stream))
     _check(st)
     return dq, dk, dv
+
+
+def fa_bwd_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, workspace, *, causal=False,
+                 scale=None, kv_len=None, stream=None):
+    """One kernel of fa_bwd into caller-allocated outputs: stage 0 writes D into the
+    workspace, 1 writes dk and dv, 2 writes dq (stages 1 and 2 need stage 0 first)."""
+    B, H, N, d = _shape(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    kv = _kv(kv_len, B, q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa_bwd_stage(int(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                              _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, scale,
+                              int(bool(causal)), _DTYPE_CODE[q.dtype], _ptr(kv),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(q.device, stream))
+    _check(st)
 
 
 def fa_fwd_partial(q, k, v, *, split_len, causal=False, scale=None, kv_len=None, out=None,

@@ -247,7 +247,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* o, const 
              const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
              float scale, int causal, int dtype, const int32_t* kv_len,
              const uint8_t* block_mask, void* workspace, size_t workspace_bytes,
-             void* stream) {
+             void* stream, int stages = 7) {
   clear_error();
   int st = check_common(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
@@ -288,7 +288,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* o, const 
   fa::BwdArgs a{q,  k,  v,  o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal ? 1 : 0,
                 dtype, kv_len, static_cast<float*>(workspace)};
   a.block_mask = block_mask;
-  hipError_t e = fa::launch_bwd(a, static_cast<hipStream_t>(stream));
+  hipError_t e = fa::launch_bwd(a, static_cast<hipStream_t>(stream), stages);
   if (e != hipSuccess) return fail(FA_EHIP, "backward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }
@@ -303,6 +303,19 @@ int fa_bwd(const void* q, const void* k, const void* v, const float* o, const vo
            size_t workspace_bytes, void* stream) {
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, kv_len,
                   nullptr, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const float* o,
+                 const void* dout, const float* lse, float* dq, float* dk, float* dv, int B,
+                 int H, int N, int d, float scale, int causal, int dtype,
+                 const int32_t* kv_len, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  if (stage < 0 || stage > 2) {
+    clear_error();
+    return fail(FA_EINVAL, "stage must be 0 (D), 1 (dK/dV) or 2 (dQ), got %d", stage);
+  }
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, kv_len,
+                  nullptr, workspace, workspace_bytes, stream, 1 << stage);
 }
 
 int fa_bwd_sparse(const void* q, const void* k, const void* v, const float* o,

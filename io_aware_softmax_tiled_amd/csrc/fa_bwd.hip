@@ -630,7 +630,7 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   return (bytes + 255) / 256 * 256;
 }
 
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages) {
   if (a.dtype == kDtypeF32) return hipErrorNotSupported;  // rejected by the API layer
   const int BH = a.B * a.H;
   const size_t rows = (size_t)BH * a.N;
@@ -646,16 +646,19 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   const int n_sb = (a.N + kSparseBlock - 1) / kSparseBlock;
 #define FA_BWD_LAUNCH2(TAG, DIM, SP)                                                         \
   do {                                                                                       \
-    hipLaunchKernelGGL((bwd_pre_kernel<TAG, DIM>), dim3(pre_blocks), dim3(kThreads), 0,      \
-                       stream, dO16, a.o, a.delta, rows);                                    \
-    hipLaunchKernelGGL((bwd_dkdv_kernel<TAG, DIM, SP>), dim3(8 * hpx * n_kblk),              \
-                       dim3(kThreads), 0, stream, q16, k16, v16, dO16, a.lse, a.delta, a.dk, \
-                       a.dv, BH, a.H, a.N, a.scale, sl2, a.causal, a.kv_len, n_kblk, hpx,    \
-                       a.block_mask, n_sb);                                                  \
-    hipLaunchKernelGGL((bwd_dq_kernel<TAG, DIM, SP>), dim3(8 * hpx * n_mblk),                \
-                       dim3(kThreads), 0, stream, q16, k16, v16, dO16, a.lse, a.delta, a.dq, \
-                       BH, a.H, a.N, a.scale, sl2, a.causal, a.kv_len, n_mblk, hpx,          \
-                       a.block_mask, n_sb);                                                  \
+    if (stages & 1)                                                                          \
+      hipLaunchKernelGGL((bwd_pre_kernel<TAG, DIM>), dim3(pre_blocks), dim3(kThreads), 0,    \
+                         stream, dO16, a.o, a.delta, rows);                                  \
+    if (stages & 2)                                                                          \
+      hipLaunchKernelGGL((bwd_dkdv_kernel<TAG, DIM, SP>), dim3(8 * hpx * n_kblk),            \
+                         dim3(kThreads), 0, stream, q16, k16, v16, dO16, a.lse, a.delta,     \
+                         a.dk, a.dv, BH, a.H, a.N, a.scale, sl2, a.causal, a.kv_len, n_kblk, \
+                         hpx, a.block_mask, n_sb);                                           \
+    if (stages & 4)                                                                          \
+      hipLaunchKernelGGL((bwd_dq_kernel<TAG, DIM, SP>), dim3(8 * hpx * n_mblk),              \
+                         dim3(kThreads), 0, stream, q16, k16, v16, dO16, a.lse, a.delta,     \
+                         a.dq, BH, a.H, a.N, a.scale, sl2, a.causal, a.kv_len, n_mblk, hpx,  \
+                         a.block_mask, n_sb);                                                \
   } while (0)
 #define FA_BWD_LAUNCH(TAG, DIM)                             \
   do {                                                      \

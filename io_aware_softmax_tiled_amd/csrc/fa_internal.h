@@ -67,6 +67,7 @@ struct MergeArgs {
   int n_splits, B, H, N, d;
 };
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+// stages: bit 0 = D (bwd_pre), bit 1 = dK/dV, bit 2 = dQ; launched in that order
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages = 7);
 
 }  // namespace fa

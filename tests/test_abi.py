@@ -30,7 +30,8 @@ def lib():
 
 
 def test_header_declares_the_api():
-    assert declared_symbols() == ["fa_bwd", "fa_bwd_sparse", "fa_bwd_workspace_size",
+    assert declared_symbols() == ["fa_bwd", "fa_bwd_sparse", "fa_bwd_stage",
+                                  "fa_bwd_workspace_size",
                                   "fa_fwd", "fa_fwd_partial", "fa_fwd_sparse",
                                   "fa_last_error", "fa_merge", "fa_split_count",
                                   "fa_status_str", "fa_version"]
@@ -237,3 +238,14 @@ def test_sparse_bwd_rejects_before_launch(lib):
 
 def test_sparse_empty_is_noop(lib):
     assert _sfwd(lib, N=0, mask=None) == FA_OK
+
+
+def test_bwd_stage_rejects_before_launch(lib):
+    args = [P, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x400000, P + 0x500000,
+            P + 0x600000, P + 0x700000, P + 0x800000, 1, 1, 64, 64, 0.125, 0, 1, None]
+    ws = lib.fa_bwd_workspace_size(1, 1, 64, 64)
+    for bad in (-1, 3, 7):
+        assert lib.fa_bwd_stage(bad, *args, P + 0x900000, ws, None) == FA_EINVAL
+    assert lib.fa_bwd_stage(1, *args, None, 0, None) == FA_EWORKSPACE
+    args[15] = 0  # f32
+    assert lib.fa_bwd_stage(0, *args, P + 0x900000, ws, None) == FA_EUNSUPPORTED

@@ -94,3 +94,31 @@ def test_bwd_deterministic():
     r2 = U.gpu_bwd(inp, dev)
     for a, b in zip(r1, r2):
         assert torch.equal(a, b)
+
+
+def test_bwd_stages_match_fa_bwd():
+    """fa_bwd_stage 0, 1, 2 give fa_bwd's results bit for bit, also with stages 1 and 2
+    on two streams."""
+    import io_aware_softmax_tiled_amd as fa
+    w, inp = workloads.custom(2, 3, 700, 128, "bf16", True, kv_range=(350, 700), seed=25)
+    dev = U.to_dev(inp)
+    o, lse, dq, dk, dv = U.gpu_bwd(inp, dev)
+    ws = torch.empty(fa.fa_bwd_workspace_size(2, 3, 700, 128), dtype=torch.uint8,
+                     device="cuda")
+    outs = [torch.full_like(dq, float("nan")) for _ in range(3)]
+    kw = dict(causal=True, scale=inp["scale"], kv_len=dev["kv_len"])
+    for st in range(3):
+        fa.fa_bwd_stage(st, dev["q"], dev["k"], dev["v"], o, dev["dout"], lse, *outs, ws, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(outs, (dq, dk, dv)):
+        assert torch.equal(a, b)
+    outs2 = [torch.full_like(dq, float("nan")) for _ in range(3)]
+    side = torch.cuda.Stream()
+    fa.fa_bwd_stage(0, dev["q"], dev["k"], dev["v"], o, dev["dout"], lse, *outs2, ws, **kw)
+    side.wait_stream(torch.cuda.current_stream())
+    fa.fa_bwd_stage(1, dev["q"], dev["k"], dev["v"], o, dev["dout"], lse, *outs2, ws, **kw)
+    fa.fa_bwd_stage(2, dev["q"], dev["k"], dev["v"], o, dev["dout"], lse, *outs2, ws,
+                    stream=side, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(outs2, (dq, dk, dv)):
+        assert torch.equal(a, b)
