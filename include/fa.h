@@ -193,6 +193,37 @@ FA_API int fa_bwd_stage(int stage, const void* q, const void* k, const void* v,
                  const int32_t* kv_len, void* workspace, size_t workspace_bytes,
                  void* stream);
 
+/*
+ * Attention with dropout on the probabilities.
+ * "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness"
+ * (summary of arXiv 2205.14135): Key ideas (kernel fusion) fuses dropout into the one
+ * attention kernel, and the FAQ on recomputation has the backward pass regenerate the
+ * dropout mask on chip from the stored state of the random generator instead of reading
+ * it from HBM. The pages name no generator; this library uses Philox4x64-10 (Salmon,
+ * Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC11), keyed by
+ * (seed, offset): the random byte of element (batch b, head h, query i, key j) is byte
+ * j % 32, little-endian, of the four 64-bit words the generator returns for the counter
+ * (i, j / 32, b*H + h, 0). With t = round(256 p) (at most 255) an element is kept iff
+ * its byte >= t, and kept probabilities are scaled by 256 / (256 - t):
+ *   o = (P * Z * 256/(256 - t)) v, lse = log-sum-exp of the undropped scaled scores.
+ * fa_bwd_dropout computes the gradients of that o with the same mask (same p, seed and
+ * offset; o and lse from fa_fwd_dropout). p must lie in [0, 1) (else FA_EINVAL); p = 0
+ * gives t = 0 and exactly fa_fwd / fa_bwd. dtype FA_BF16 or FA_F16 (FA_F32 is
+ * FA_EUNSUPPORTED); other arguments, layouts and errors as fa_fwd / fa_bwd. The mask is
+ * a pure function of (seed, offset, b*H + h, i, j): calls with the same key reproduce it,
+ * whatever the launch order.
+ */
+FA_API int fa_fwd_dropout(const void* q, const void* k, const void* v, float* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal, int dtype,
+                   const int32_t* kv_len, float p, uint64_t seed, uint64_t offset,
+                   void* stream);
+
+FA_API int fa_bwd_dropout(const void* q, const void* k, const void* v, const float* o,
+                   const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                   int B, int H, int N, int d, float scale, int causal, int dtype,
+                   const int32_t* kv_len, float p, uint64_t seed, uint64_t offset,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 FA_API const char* fa_status_str(int status);
 

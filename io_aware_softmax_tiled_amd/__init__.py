@@ -32,7 +32,8 @@ import os
 import torch
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_split_count", "fa_fwd_partial",
-           "fa_merge", "fa_fwd_sparse", "fa_bwd_sparse", "FA_SPARSE_BLOCK", "fa_status_str", "fa_last_error", "fa_version", "FaError", "lib_path",
+           "fa_merge", "fa_fwd_sparse", "fa_bwd_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
+           "FA_SPARSE_BLOCK", "fa_status_str", "fa_last_error", "fa_version", "FaError", "lib_path",
            "load_library",
            "FA_F32", "FA_BF16", "FA_F16"]
 
@@ -87,6 +88,13 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
                                   i32, i32, vp, vp, vp, sz, vp]
     lib.fa_bwd_sparse.restype = i32
+    u64 = ctypes.c_uint64
+    lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, i32, vp,
+                                   f32, u64, u64, vp]
+    lib.fa_fwd_dropout.restype = i32
+    lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                   i32, i32, vp, f32, u64, u64, vp, sz, vp]
+    lib.fa_bwd_dropout.restype = i32
     lib.fa_status_str.argtypes = [i32]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -313,5 +321,61 @@ def fa_bwd_sparse(q, k, v, o, dout, lse, block_mask, *, causal=False, scale=None
                                int(bool(causal)), _DTYPE_CODE[q.dtype], _ptr(kv), _ptr(bm),
                                _ptr(workspace), workspace.numel() * workspace.element_size(),
                                _stream(q.device, stream))
+    _check(st)
+    return dq, dk, dv
+
+
+def _key(seed, offset):
+    seed, offset = int(seed), int(offset)
+    if not (0 <= seed < 1 << 64 and 0 <= offset < 1 << 64):
+        raise ValueError("seed and offset are unsigned 64-bit integers")
+    return seed, offset
+
+
+def fa_fwd_dropout(q, k, v, *, p, seed, offset=0, causal=False, scale=None, kv_len=None,
+                   out=None, lse=None, stream=None):
+    """Forward with dropout p on the probabilities, mask drawn from Philox4x64-10 keyed by
+    (seed, offset): returns (o, lse), lse that of the undropped scores."""
+    seed, offset = _key(seed, offset)
+    B, H, N, d = _shape(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    kv = _kv(kv_len, B, q.device)
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
+                                scale, int(bool(causal)), _DTYPE_CODE[q.dtype], _ptr(kv),
+                                float(p), seed, offset, _stream(q.device, stream))
+    _check(st)
+    return o, lse_t
+
+
+def fa_bwd_dropout(q, k, v, o, dout, lse, *, p, seed, offset=0, causal=False, scale=None,
+                   kv_len=None, workspace=None, stream=None):
+    """Backward of sum(dout * O) for O from fa_fwd_dropout with the same p, seed and offset
+    (the mask is regenerated, not stored): returns (dq, dk, dv), float32 [B,H,N,d]."""
+    seed, offset = _key(seed, offset)
+    B, H, N, d = _shape(q, k, v)
+    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
+        raise ValueError("dout must match q in shape and dtype and be contiguous")
+    if o.dtype != torch.float32 or lse.dtype != torch.float32:
+        raise ValueError("o and lse must be the float32 outputs of fa_fwd_dropout")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    kv = _kv(kv_len, B, q.device)
+    ws_bytes = fa_bwd_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, scale,
+                                int(bool(causal)), _DTYPE_CODE[q.dtype], _ptr(kv), float(p),
+                                seed, offset, _ptr(workspace),
+                                workspace.numel() * workspace.element_size(),
+                                _stream(q.device, stream))
     _check(st)
     return dq, dk, dv

@@ -98,9 +98,25 @@ int check_sparse(int N, int dtype, const uint8_t* block_mask) {
   return FA_OK;
 }
 
+// Dropout of the probabilities: byte threshold t (-1: none) and the generator key.
+struct Drop {
+  int t = -1;
+  uint64_t seed = 0, offset = 0;
+};
+
+// t = round(256 p), keep iff the element's random byte >= t.
+int check_dropout(int dtype, float p, Drop* out) {
+  if (dtype == FA_F32)
+    return fail(FA_EUNSUPPORTED, "attention with dropout takes bf16 or f16 inputs, not f32");
+  if (!(p >= 0.0f && p < 1.0f)) return fail(FA_EINVAL, "dropout p=%g is not in [0, 1)", p);
+  const int t = (int)std::floor(256.0 * (double)p + 0.5);
+  out->t = t < 255 ? t : 255;
+  return FA_OK;
+}
+
 int fwd_impl(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
              int N, int d, float scale, int causal, int dtype, const int32_t* kv_len,
-             const uint8_t* block_mask, void* stream) {
+             const uint8_t* block_mask, void* stream, const Drop& drop = Drop()) {
   clear_error();
   int st = check_common(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
@@ -127,6 +143,9 @@ int fwd_impl(const void* q, const void* k, const void* v, float* o, float* lse, 
 
   fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal ? 1 : 0, dtype, kv_len};
   a.block_mask = block_mask;
+  a.drop_t = drop.t;
+  a.seed = drop.seed;
+  a.offset = drop.offset;
   hipError_t e = fa::launch_fwd(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_EHIP, "forward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
@@ -152,6 +171,22 @@ int fa_fwd_sparse(const void* q, const void* k, const void* v, float* o, float* 
   if (st != FA_OK) return st;
   return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, kv_len, block_mask,
                   stream);
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                   int H, int N, int d, float scale, int causal, int dtype,
+                   const int32_t* kv_len, float p, uint64_t seed, uint64_t offset,
+                   void* stream) {
+  clear_error();
+  int st = check_common(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  Drop drop;
+  st = check_dropout(dtype, p, &drop);
+  if (st != FA_OK) return st;
+  drop.seed = seed;
+  drop.offset = offset;
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, kv_len, nullptr, stream,
+                  drop);
 }
 
 int fa_split_count(int N, int split_len) {
@@ -247,7 +282,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* o, const 
              const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
              float scale, int causal, int dtype, const int32_t* kv_len,
              const uint8_t* block_mask, void* workspace, size_t workspace_bytes,
-             void* stream, int stages = 7) {
+             void* stream, int stages = 7, const Drop& drop = Drop()) {
   clear_error();
   int st = check_common(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
@@ -288,6 +323,9 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* o, const 
   fa::BwdArgs a{q,  k,  v,  o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal ? 1 : 0,
                 dtype, kv_len, static_cast<float*>(workspace)};
   a.block_mask = block_mask;
+  a.drop_t = drop.t;
+  a.seed = drop.seed;
+  a.offset = drop.offset;
   hipError_t e = fa::launch_bwd(a, static_cast<hipStream_t>(stream), stages);
   if (e != hipSuccess) return fail(FA_EHIP, "backward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
@@ -330,6 +368,23 @@ int fa_bwd_sparse(const void* q, const void* k, const void* v, const float* o,
   if (st != FA_OK) return st;
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, kv_len,
                   block_mask, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const float* o,
+                   const void* dout, const float* lse, float* dq, float* dk, float* dv, int B,
+                   int H, int N, int d, float scale, int causal, int dtype,
+                   const int32_t* kv_len, float p, uint64_t seed, uint64_t offset,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  int st = check_common(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  Drop drop;
+  st = check_dropout(dtype, p, &drop);
+  if (st != FA_OK) return st;
+  drop.seed = seed;
+  drop.offset = offset;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, kv_len,
+                  nullptr, workspace, workspace_bytes, stream, 7, drop);
 }
 
 }  // extern "C"

@@ -88,14 +88,19 @@ constexpr int kBQ = 64;   // queries per tile (two 32-query halves)
 constexpr int kSparseBlock = 128;
 constexpr int kSparseMaxBlocks = 2048;  // blocks per row/column of the mask (N <= 2^18)
 
-template <typename T, int D, bool kSparse>
+// kDropout: the probabilities carry the forward pass's dropout mask Z (regenerated here
+// from the same Philox4x64-10 blocks: element (i, j) of head bh is byte j % 32 of the
+// block at counter (i, j / 32, bh, 0), key (seed, offset); kept iff >= drop_t):
+// dV = (P Z / keep)^T dO, dP = (Z / keep) (dO V^T), dS = P (dP - D).
+template <typename T, int D, bool kSparse, bool kDropout>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ delta, float* __restrict__ dK,
     float* __restrict__ dV, int BH, int H, int N, float scale, float sl2, int causal,
     const int* __restrict__ kv_len, int n_kblk, int heads_per_xcd,
-    const uint8_t* __restrict__ bmask, int n_sb) {
+    const uint8_t* __restrict__ bmask, int n_sb, uint64_t seed, uint64_t offset, int drop_t,
+    float keep_scale) {
   constexpr int kKC = D / 16;
   constexpr int kDB = D / 32;
   constexpr int kCPR = D / 8;                        // 16-byte chunks per row
@@ -109,6 +114,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) float St1[2 * kBQ];
   __shared__ uint16_t tlist[kSparse ? 2 * kSparseMaxBlocks : 1];  // enabled query tiles
   __shared__ int tlist_len;
+  // dropout: each wave's random bytes of the current tile, [query][its 32 keys]
+  __shared__ __attribute__((aligned(16))) uint8_t zbuf[kDropout ? 4 * kBQ * 32 : 16];
 
   const WgPos pos = wg_position(heads_per_xcd, blockIdx.x);
   const int kblk = pos.blk;  // key block 0 has the most query tiles under a causal mask
@@ -274,6 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       s[r] = hide ? -INFINITY : s[r];
     }
   };
+  FA_LDS uint8_t* zw = (FA_LDS uint8_t*)zbuf + (kDropout ? wave * kBQ * 32 : 0);  // wave bytes
   // P and dS for half `hf` (masked scores are -inf, so P = dS = 0 there), packed fp16
   auto p_ds = [&](const FA_LDS float* Stc, int hf, const f32x16& s, const f32x16& dp,
                   uint32_t (&pp)[8], uint32_t (&dsp)[8]) {
@@ -291,8 +299,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         const float lq = j < 4 ? l0[j] : l1[j - 4];
         const float dq = j < 4 ? d0[j] : d1[j - 4];
         const float pj = exp2_fast(fmaf(s[r], sl2, -lq));
-        p[j] = pj;
-        ds[j] = pj * (dp[r] - dq);
+        if constexpr (kDropout) {
+          // byte of (query qb + j of the tile, this lane's key)
+          const bool keep = (int)zw[(qb + j) * 32 + li] >= drop_t;
+          p[j] = keep ? pj : 0.f;                      // dV takes P Z (1/keep at the end)
+          ds[j] = pj * ((keep ? dp[r] * keep_scale : 0.f) - dq);
+        } else {
+          p[j] = pj;
+          ds[j] = pj * (dp[r] - dq);
+        }
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -355,6 +370,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bool active = !wave_dead && !(causal && kw0 > q0 + kBQ - 1);
     const bool need_mask =
         (causal && kw0 + 31 > q0) || (q0 + kBQ > N) || (kw0 + 32 > kv_lim);
+    if (kDropout && active) {
+      // lane l generates the 32 bytes of (query q0 + l, this wave's 32 keys) and stores
+      // them for the wave; each lane then reads the bytes of its own key
+      const Philox4x64 ph = philox4x64((uint64_t)(q0 + lane), (uint64_t)(kw0 >> 5),
+                                       (uint64_t)bh, 0ull, seed, offset);
+      lds_write16(zw + lane * 32, u32x4{(uint32_t)ph.w[0], (uint32_t)(ph.w[0] >> 32),
+                                        (uint32_t)ph.w[1], (uint32_t)(ph.w[1] >> 32)});
+      lds_write16(zw + lane * 32 + 16, u32x4{(uint32_t)ph.w[2], (uint32_t)(ph.w[2] >> 32),
+                                             (uint32_t)ph.w[3], (uint32_t)(ph.w[3] >> 32)});
+    }
     if (active) {
       f32x16 s0, dp0, s1, dp1;
       uint32_t pp0[8], ds0[8], pp1[8], ds1[8];
@@ -411,8 +436,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         const int d0 = 32 * db + 8 * a4 + 4 * hh;
         const f32x4 kk = {scale * dkacc[db][4 * a4], scale * dkacc[db][4 * a4 + 1],
                           scale * dkacc[db][4 * a4 + 2], scale * dkacc[db][4 * a4 + 3]};
-        const f32x4 vv = {dvacc[db][4 * a4], dvacc[db][4 * a4 + 1], dvacc[db][4 * a4 + 2],
-                          dvacc[db][4 * a4 + 3]};
+        const float vs = kDropout ? keep_scale : 1.0f;
+        const f32x4 vv = {vs * dvacc[db][4 * a4], vs * dvacc[db][4 * a4 + 1],
+                          vs * dvacc[db][4 * a4 + 2], vs * dvacc[db][4 * a4 + 3]};
         *reinterpret_cast<f32x4*>(dkr + d0) = kk;
         *reinterpret_cast<f32x4*>(dvr + d0) = vv;
       }
@@ -426,15 +452,16 @@ constexpr int kBM = 128;  // queries per workgroup
 constexpr int kBN = 64;   // keys per tile
 
 // kSparse: this workgroup's 128 queries are one query block of bmask; key tiles in
-// disabled key blocks are skipped.
-template <typename T, int D, bool kSparse>
+// disabled key blocks are skipped. kDropout: as in the dK/dV kernel, dP = (Z / keep) dP~.
+template <typename T, int D, bool kSparse, bool kDropout>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ delta, float* __restrict__ dQ,
     int BH, int H, int N, float scale, float sl2, int causal,
     const int* __restrict__ kv_len, int n_mblk, int heads_per_xcd,
-    const uint8_t* __restrict__ bmask, int n_sb) {
+    const uint8_t* __restrict__ bmask, int n_sb, uint64_t seed, uint64_t offset, int drop_t,
+    float keep_scale) {
   constexpr int kKC = D / 16;
   constexpr int kDB = D / 32;
   constexpr int kCPR = D / 8;
@@ -576,11 +603,26 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         }
       }
       uint32_t dsk[8];
+      uint64_t rnd[2] = {0, 0};
+      if constexpr (kDropout) {
+        // registers 8c .. 8c+7 hold keys n0 + 32 sub + 16c + 8 hh + 0..7: the bytes of
+        // word 2c + hh of the sub-block's Philox block
+        const Philox4x64 ph = philox4x64((uint64_t)qrow, (uint64_t)((n0 + 32 * sub) >> 5),
+                                         (uint64_t)bh, 0ull, seed, offset);
+        rnd[0] = hh ? ph.w[1] : ph.w[0];
+        rnd[1] = hh ? ph.w[3] : ph.w[2];
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float p0 = exp2_fast(fmaf(st[2 * i], sl2, -lse2));
         const float p1 = exp2_fast(fmaf(st[2 * i + 1], sl2, -lse2));
-        dsk[i] = Mfma<F16>::pack(p0 * (dpt[2 * i] - dlt), p1 * (dpt[2 * i + 1] - dlt));
+        float dp0 = dpt[2 * i], dp1 = dpt[2 * i + 1];
+        if constexpr (kDropout) {
+          const uint64_t wv = rnd[i >> 2] >> (16 * (i & 3));
+          dp0 = (int)(wv & 0xff) >= drop_t ? dp0 * keep_scale : 0.f;
+          dp1 = (int)((wv >> 8) & 0xff) >= drop_t ? dp1 * keep_scale : 0.f;
+        }
+        dsk[i] = Mfma<F16>::pack(p0 * (dp0 - dlt), p1 * (dp1 - dlt));
       }
       // dQ^T += K^T dS^T: two 16-key steps; K^T through the transposing read
 #pragma unroll
@@ -644,26 +686,29 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages) {
   const auto* v16 = static_cast<const uint16_t*>(a.v);
   const auto* dO16 = static_cast<const uint16_t*>(a.dout);
   const int n_sb = (a.N + kSparseBlock - 1) / kSparseBlock;
-#define FA_BWD_LAUNCH2(TAG, DIM, SP)                                                         \
+  const bool dropout = a.drop_t >= 0;
+  const float keep_scale = dropout ? 256.0f / (float)(256 - a.drop_t) : 1.0f;
+#define FA_BWD_LAUNCH2(TAG, DIM, SP, DR)                                                     \
   do {                                                                                       \
     if (stages & 1)                                                                          \
       hipLaunchKernelGGL((bwd_pre_kernel<TAG, DIM>), dim3(pre_blocks), dim3(kThreads), 0,    \
                          stream, dO16, a.o, a.delta, rows);                                  \
     if (stages & 2)                                                                          \
-      hipLaunchKernelGGL((bwd_dkdv_kernel<TAG, DIM, SP>), dim3(8 * hpx * n_kblk),            \
+      hipLaunchKernelGGL((bwd_dkdv_kernel<TAG, DIM, SP, DR>), dim3(8 * hpx * n_kblk),        \
                          dim3(kThreads), 0, stream, q16, k16, v16, dO16, a.lse, a.delta,     \
                          a.dk, a.dv, BH, a.H, a.N, a.scale, sl2, a.causal, a.kv_len, n_kblk, \
-                         hpx, a.block_mask, n_sb);                                           \
+                         hpx, a.block_mask, n_sb, a.seed, a.offset, a.drop_t, keep_scale);   \
     if (stages & 4)                                                                          \
-      hipLaunchKernelGGL((bwd_dq_kernel<TAG, DIM, SP>), dim3(8 * hpx * n_mblk),              \
+      hipLaunchKernelGGL((bwd_dq_kernel<TAG, DIM, SP, DR>), dim3(8 * hpx * n_mblk),          \
                          dim3(kThreads), 0, stream, q16, k16, v16, dO16, a.lse, a.delta,     \
                          a.dq, BH, a.H, a.N, a.scale, sl2, a.causal, a.kv_len, n_mblk, hpx,  \
-                         a.block_mask, n_sb);                                                \
+                         a.block_mask, n_sb, a.seed, a.offset, a.drop_t, keep_scale);        \
   } while (0)
-#define FA_BWD_LAUNCH(TAG, DIM)                             \
-  do {                                                      \
-    if (a.block_mask != nullptr) FA_BWD_LAUNCH2(TAG, DIM, true); \
-    else FA_BWD_LAUNCH2(TAG, DIM, false);                   \
+#define FA_BWD_LAUNCH(TAG, DIM)                                          \
+  do {                                                                   \
+    if (a.block_mask != nullptr) FA_BWD_LAUNCH2(TAG, DIM, true, false);  \
+    else if (dropout) FA_BWD_LAUNCH2(TAG, DIM, false, true);             \
+    else FA_BWD_LAUNCH2(TAG, DIM, false, false);                         \
   } while (0)
   if (a.dtype == kDtypeBF16) {
     if (a.d == 64) FA_BWD_LAUNCH(BF16, 64); else FA_BWD_LAUNCH(BF16, 128);

@@ -68,6 +68,11 @@ constexpr int kThreads = 256;
 // list below) and streams only those tiles; a wave whose own query block leaves a
 // listed key block disabled masks it.
 // In both modes a row that sees no key gets O = 0 and LSE = -inf.
+// kMode 3, dropout: the normalised probabilities are multiplied by Z / keep, Z_ij = 1
+// iff random byte (i, j) >= drop_t, keep = (256 - drop_t) / 256 (keep_scale = 1/keep);
+// byte (i, j) of head bh is byte j % 32 of the Philox4x64-10 block at counter
+// (i, j / 32, bh, 0) and key (seed, offset). The statistics (and LSE) are those of the
+// undropped scores.
 constexpr int kSparseBlock = 128;
 constexpr int kSparseMaxBlocks = 2048;  // key blocks per row of the mask (N <= 2^18)
 
@@ -78,9 +83,10 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
     int BH, int H, int N, float scale, float sl2, int causal,
     const int* __restrict__ kv_len, int n_mblk, int heads_per_xcd, int split_len,
     int per_split, size_t o_stride, size_t lse_stride, const uint8_t* __restrict__ bmask,
-    int n_sb) {
+    int n_sb, uint64_t seed, uint64_t offset, int drop_t, float keep_scale) {
   constexpr bool kPartial = kMode == 1;
   constexpr bool kSparse = kMode == 2;
+  constexpr bool kDropout = kMode == 3;
   constexpr bool kGuard = kMode != 0;  // rows may see no key at all
   constexpr int kTileBytes = kBN * D * 2;              // one K or V tile
   constexpr int kKC = D / 16;                          // 16-wide k-steps over head_dim
@@ -296,8 +302,19 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
     for (int c = 0; c < kKC; ++c) acc = Mfma<T>::run(kf[c], qf[c], acc);
     return acc;
   };
-  // P = exp2(s*scale*log2e - m_ref*scale*log2e), rounded to fp16, and its row sum
-  auto expo = [&](const f32x16& s, uint32_t (&pk)[8]) {
+  // P = exp2(s*scale*log2e - m_ref*scale*log2e), rounded to fp16, and its row sum;
+  // with dropout the product takes P * Z (the scale 1/keep is applied at the end) while
+  // the row sum takes P. Sub-block sb: keys 32*sb .. 32*sb+31; this lane's register r
+  // holds key 32*sb + 16*(r/8) + 8*hh + r%8, i.e. byte r%8 of word 2*(r/8) + hh of the
+  // sub-block's Philox block.
+  auto expo = [&](const f32x16& s, uint32_t (&pk)[8], int sb) {
+    uint64_t rnd[2] = {0, 0};
+    if constexpr (kDropout) {
+      const Philox4x64 ph = philox4x64((uint64_t)qrow, (uint64_t)sb, (uint64_t)pos.bh, 0ull,
+                                       seed, offset);
+      rnd[0] = hh ? ph.w[1] : ph.w[0];
+      rnd[1] = hh ? ph.w[3] : ph.w[2];
+    }
     // (a row that has seen no visible key yet -- possible in a split or a sparse
     // pattern -- keeps
     // m_ref = -inf; its scores are all -inf and must give P = 0, not NaN)
@@ -308,6 +325,13 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
       const float p1 = exp2_fast(fmaf(s[2 * i + 1], sl2, nms));
       pk[i] = Mfma<F16>::pack(p0, p1);
       lsum = Mfma<F16>::dot_ones(pk[i], lsum);
+      if constexpr (kDropout) {
+        // registers 2i, 2i+1: bytes (2i)%8 and (2i+1)%8 of word i/4
+        const uint64_t wv = rnd[i >> 2] >> (16 * (i & 3));
+        const bool keep0 = (int)(wv & 0xff) >= drop_t;
+        const bool keep1 = (int)((wv >> 8) & 0xff) >= drop_t;
+        pk[i] = Mfma<F16>::pack(keep0 ? p0 : 0.f, keep1 ? p1 : 0.f);
+      }
     }
   };
   // two 16-key steps of O^T += V^T P^T from the V^T fragments in vf
@@ -413,7 +437,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
 
     uint32_t pk[8];
     f32x16 Sn = scores();        // sub-block 2t+1 (K fragments read beforehand)
-    expo(S, pk);                 // P of sub-block 2t
+    expo(S, pk, 2 * t);          // P of sub-block 2t
     read_v(Va, 0);
     hint_a(std::integral_constant<int, 48 + 12 * kVChunks + 12>{});  // with the V conversion and the load addresses
     pin(pk);
@@ -425,7 +449,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
     rescale(mx);
 
     S = scores();                // sub-block 2t+2
-    expo(Sn, pk);                // P of sub-block 2t+1
+    expo(Sn, pk, 2 * t + 1);     // P of sub-block 2t+1
     read_v(Va, 1);
     hint_a(std::integral_constant<int, 48>{});
     pin(pk);
@@ -453,7 +477,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   if (qrow < N) {
     // a row with no visible key (split or sparse pattern: ltot = 0) gets O = 0, LSE = -inf
     const bool empty = kGuard && !(ltot > 0.f);
-    const float inv = empty ? 0.f : 1.0f / ltot;
+    const float inv = empty ? 0.f : (kDropout ? keep_scale : 1.0f) / ltot;
     float* orow = O + head + (size_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
@@ -654,11 +678,14 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   const int n_splits = partial ? (a.N + a.split_len - 1) / a.split_len : 1;
   const size_t o_stride = (size_t)BH * a.N * a.d, lse_stride = (size_t)BH * a.N;
   const int n_sb = (a.N + kSparseBlock - 1) / kSparseBlock;
+  const bool dropout = a.drop_t >= 0;
+  const float keep_scale = dropout ? 256.0f / (float)(256 - a.drop_t) : 1.0f;
 #define FA_LAUNCH16W(TAG, DIM, WV, MODE)                                                   \
   hipLaunchKernelGGL((fwd_kernel_16<TAG, DIM, WV, MODE>), dim3(g.blocks * n_splits),        \
                      dim3(WV * 64), 0, stream, q16, k16, v16, a.o, a.lse, BH, a.H, a.N,     \
                      a.scale, sl2, a.causal, a.kv_len, g.n_mblk, g.heads_per_xcd,           \
-                     a.split_len, g.blocks, o_stride, lse_stride, a.block_mask, n_sb)
+                     a.split_len, g.blocks, o_stride, lse_stride, a.block_mask, n_sb,      \
+                     a.seed, a.offset, a.drop_t, keep_scale)
   // head_dim 128 always runs 8 waves (its LDS use allows one workgroup per CU)
 #define FA_LAUNCH16(TAG, DIM, MODE)                                 \
   do {                                                              \
@@ -669,6 +696,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   do {                                               \
     if (partial) FA_LAUNCH16(TAG, DIM, 1);           \
     else if (sparse) FA_LAUNCH16(TAG, DIM, 2);       \
+    else if (dropout) FA_LAUNCH16(TAG, DIM, 3);      \
     else FA_LAUNCH16(TAG, DIM, 0);                   \
   } while (0)
 #define FA_LAUNCH32(DIM)                                                                  \
@@ -681,7 +709,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   } else if (a.dtype == kDtypeF16) {
     if (a.d == 64) FA_LAUNCH16P(F16, 64); else FA_LAUNCH16P(F16, 128);
   } else {
-    if (partial || sparse) return hipErrorNotSupported;  // rejected by the API layer
+    if (partial || sparse || dropout) return hipErrorNotSupported;  // rejected by the API
     if (a.d == 64) FA_LAUNCH32(64); else FA_LAUNCH32(128);
   }
 #undef FA_LAUNCH16P

@@ -39,6 +39,8 @@ from .dropout import (  # noqa: F401
     dropout_threshold,
     random_bytes,
     keep_mask,
+    head_forward_dropout,
+    head_backward_dropout,
     attention_forward_dropout,
     attention_backward_dropout,
 )

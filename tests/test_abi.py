@@ -30,9 +30,9 @@ def lib():
 
 
 def test_header_declares_the_api():
-    assert declared_symbols() == ["fa_bwd", "fa_bwd_sparse", "fa_bwd_stage",
+    assert declared_symbols() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_sparse", "fa_bwd_stage",
                                   "fa_bwd_workspace_size",
-                                  "fa_fwd", "fa_fwd_partial", "fa_fwd_sparse",
+                                  "fa_fwd", "fa_fwd_dropout", "fa_fwd_partial", "fa_fwd_sparse",
                                   "fa_last_error", "fa_merge", "fa_split_count",
                                   "fa_status_str", "fa_version"]
 
@@ -249,3 +249,47 @@ def test_bwd_stage_rejects_before_launch(lib):
     assert lib.fa_bwd_stage(1, *args, None, 0, None) == FA_EWORKSPACE
     args[15] = 0  # f32
     assert lib.fa_bwd_stage(0, *args, P + 0x900000, ws, None) == FA_EUNSUPPORTED
+
+
+# ---- dropout -------------------------------------------------------------------------
+
+def _dfwd(lib, p=0.1, N=256, dtype=1, q=P, seed=1, offset=0):
+    return lib.fa_fwd_dropout(q, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x700000, 1,
+                              1, N, 64, 0.125, 0, dtype, None, p, seed, offset, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(p=-0.01), FA_EINVAL),
+    (dict(p=1.0), FA_EINVAL),
+    (dict(p=float("nan")), FA_EINVAL),
+    (dict(p=float("inf")), FA_EINVAL),
+    (dict(dtype=0), FA_EUNSUPPORTED),
+    (dict(q=None), FA_EINVAL),
+])
+def test_dropout_fwd_rejects_before_launch(lib, kw, code):
+    assert _dfwd(lib, **kw) == code
+    assert fa.fa_last_error() != ""
+
+
+def test_dropout_empty_is_noop(lib):
+    assert _dfwd(lib, N=0, seed=(1 << 64) - 1, offset=(1 << 64) - 1) == FA_OK
+
+
+def test_dropout_bwd_rejects_before_launch(lib):
+    args = [P, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x400000, P + 0x500000,
+            P + 0x600000, P + 0x700000, P + 0x800000, 1, 1, 256, 64, 0.125, 0, 1, None]
+    ws = lib.fa_bwd_workspace_size(1, 1, 256, 64)
+    assert lib.fa_bwd_dropout(*args, 1.5, 1, 0, P + 0xa00000, ws, None) == FA_EINVAL
+    assert lib.fa_bwd_dropout(*args, 0.1, 1, 0, None, 0, None) == FA_EWORKSPACE
+    assert lib.fa_bwd_dropout(*args[:15], 0, None, 0.1, 1, 0, P + 0xa00000, ws,
+                              None) == FA_EUNSUPPORTED
+    assert lib.fa_bwd_dropout(*args[:15], 1, None, 0.1, 1, 0, P + 0x600000 + 16, ws,
+                              None) == FA_EINVAL   # workspace overlaps dq
+
+
+def test_dropout_binding_checks_key():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    for seed, offset in ((-1, 0), (0, 1 << 64)):
+        with pytest.raises(ValueError):
+            fa.fa_fwd_dropout(q, q, q, p=0.1, seed=seed, offset=offset)
