@@ -18,7 +18,7 @@ split             Split-KV: attention over contiguous key ranges (normalised par
                   of partials by the incremental softmax tracking rule.
 sparse            Block-sparse attention: the definition with a block mask over
                   query/key blocks (empty rows O = 0, LSE = -inf) and its gradient.
-dropout           Dropout on the probabilities with the counter-based Philox4x64-10
+dropout           Dropout on the probabilities with the counter-based Philox4x32-10
                   generator (the mask replayed from (seed, offset)), and its gradient.
 
 Every function is pinned by tests in tests/test_oracle_*.py against closed forms,
@@ -35,7 +35,7 @@ from .attention import (  # noqa: F401
     attention_backward_heads,
 )
 from .dropout import (  # noqa: F401
-    philox4x64,
+    philox4x32,
     dropout_threshold,
     random_bytes,
     keep_mask,

@@ -9,19 +9,22 @@ Sources:
   kernel; the FAQ says the method keeps, besides O and the softmax statistics, the state
   of a pseudo-random generator so the dropout mask can be regenerated on chip in the
   backward pass. The page names no generator.
-- The generator chosen here is the published counter-based Philox4x64-10 (J. K. Salmon,
+- The generator chosen here is the published counter-based Philox4x32-10 (J. K. Salmon,
   M. A. Moraes, R. O. Dror, D. E. Shaw, "Parallel random numbers: as easy as 1, 2, 3",
-  SC11): 10 rounds over a 4 x 64-bit counter with a 2 x 64-bit key; each round
-  multiplies two counter words by fixed constants, keeps both halves of the 128-bit
+  SC11): 10 rounds over a 4 x 32-bit counter with a 2 x 32-bit key; each round
+  multiplies two counter words by fixed constants, keeps both halves of the 64-bit
   products and mixes them with the other words and the round key; the key advances by
   fixed Weyl increments between rounds.
 
 Readings (where the pages are silent):
 - Dropout acts on the normalised probabilities: O = (P * Z / keep) V with Z_ij in {0,1};
   the softmax statistics (and LSE) are those of the undropped scores.
-- Random byte of element (b, h, i, j): the Philox4x64-10 block at counter
-  (i, j >> 5, b*H + h, 0) with key (seed, offset) gives four 64-bit words; their 32
-  little-endian bytes serve the 32 keys j = 32*(j >> 5) ... +31, key j taking byte j & 31.
+- Random byte of element (b, h, i, j): keys fall in groups of 32 (g = j >> 5, u = j & 31).
+  The group's 32 bytes come from two Philox4x32-10 blocks, at counters (i, 2g, b*H + h,
+  offset) and (i, 2g + 1, b*H + h, offset) with key (seed mod 2^32, seed >> 32); each
+  block gives 16 bytes (its four words, little-endian). Key u takes block 2g + ((u >> 3)
+  & 1), byte 8*(u >> 4) + (u & 7): keys 0-7 and 16-23 of the group read bytes 0-7 and
+  8-15 of the first block, keys 8-15 and 24-31 those of the second.
 - p is quantised to t = round(256 p) (0 <= t <= 255); Z_ij = 1 iff the byte >= t; the
   keep probability is (256 - t)/256 and the kept probabilities are scaled by its inverse
   256/(256 - t), so E[Z / keep] = 1 exactly.
@@ -35,35 +38,24 @@ import numpy as np
 
 from .attention import allowed_mask
 
-_M0, _M1 = np.uint64(0xD2E7470EE14C6C93), np.uint64(0xCA5A826395121157)
-_W0, _W1 = np.uint64(0x9E3779B97F4A7C15), np.uint64(0xBB67AE8584CAA73B)
+_M0, _M1 = np.uint64(0xD2511F53), np.uint64(0xCD9E8D57)
+_W0, _W1 = np.uint64(0x9E3779B9), np.uint64(0xBB67AE85)
 _LO32 = np.uint64(0xFFFFFFFF)
 _S32 = np.uint64(32)
 
 
-def _mulhilo(a, m):
-    """(hi, lo) 64-bit halves of the 128-bit product a * m (uint64 arrays)."""
-    a0, a1 = a & _LO32, a >> _S32
-    m0, m1 = m & _LO32, m >> _S32
-    p00, p01, p10, p11 = a0 * m0, a0 * m1, a1 * m0, a1 * m1
-    mid = (p00 >> _S32) + (p01 & _LO32) + (p10 & _LO32)
-    hi = p11 + (p01 >> _S32) + (p10 >> _S32) + (mid >> _S32)
-    return hi, a * m
-
-
-def philox4x64(c0, c1, c2, c3, k0, k1, rounds=10):
-    """Philox4x64 block function on uint64 arrays (broadcast): returns four uint64 words."""
-    with np.errstate(over="ignore"):
-        x0, x1, x2, x3 = (np.asarray(c, dtype=np.uint64) for c in (c0, c1, c2, c3))
-        k0 = np.asarray(k0, dtype=np.uint64)
-        k1 = np.asarray(k1, dtype=np.uint64)
-        for r in range(rounds):
-            if r:
-                k0, k1 = k0 + _W0, k1 + _W1
-            hi0, lo0 = _mulhilo(x0, _M0)
-            hi1, lo1 = _mulhilo(x2, _M1)
-            x0, x1, x2, x3 = hi1 ^ x1 ^ k0, lo1, hi0 ^ x3 ^ k1, lo0
-    return x0, x1, x2, x3
+def philox4x32(c0, c1, c2, c3, k0, k1, rounds=10):
+    """Philox4x32 block function on arrays of 32-bit values (held in uint64, broadcast):
+    returns the four output words as uint32 arrays."""
+    x0, x1, x2, x3, k0, k1 = (np.asarray(c, dtype=np.uint64) & _LO32
+                              for c in (c0, c1, c2, c3, k0, k1))
+    for r in range(rounds):
+        if r:
+            k0, k1 = (k0 + _W0) & _LO32, (k1 + _W1) & _LO32
+        p0 = x0 * _M0                      # exact: both factors are below 2^32
+        p1 = x2 * _M1
+        x0, x1, x2, x3 = (p1 >> _S32) ^ x1 ^ k0, p1 & _LO32, (p0 >> _S32) ^ x3 ^ k1, p0 & _LO32
+    return tuple(x.astype(np.uint32) for x in (x0, x1, x2, x3))
 
 
 def dropout_threshold(p: float) -> int:
@@ -73,14 +65,25 @@ def dropout_threshold(p: float) -> int:
     return min(255, int(np.floor(256.0 * p + 0.5)))
 
 
+def _check_key(seed: int, offset: int):
+    if not (0 <= seed < 1 << 64 and 0 <= offset < 1 << 32):
+        raise ValueError("seed is an unsigned 64-bit and offset an unsigned 32-bit integer")
+
+
 def random_bytes(n_q: int, n_k: int, bh: int, seed: int, offset: int) -> np.ndarray:
     """uint8 [n_q, n_k]: the random byte of every (query, key) element of head bh."""
+    _check_key(seed, offset)
+    n_blk = 2 * (-(-n_k // 32))
     i = np.arange(n_q, dtype=np.uint64)[:, None]
-    jb = np.arange(-(-n_k // 32), dtype=np.uint64)[None, :]
-    words = philox4x64(i, jb, np.uint64(bh), np.uint64(0), np.uint64(seed), np.uint64(offset))
-    w = np.stack(np.broadcast_arrays(*words), axis=-1)          # [n_q, n_jb, 4] uint64
-    b = w.astype("<u8").view(np.uint8).reshape(n_q, -1)          # little-endian bytes
-    return b[:, :n_k]
+    jb = np.arange(n_blk, dtype=np.uint64)[None, :]
+    words = philox4x32(i, jb, bh, offset, seed & 0xFFFFFFFF, seed >> 32)
+    w = np.stack(np.broadcast_arrays(*words), axis=-1).astype("<u4")    # [n_q, n_blk, 4]
+    blk_bytes = w.view(np.uint8).reshape(n_q, n_blk, 16)
+    j = np.arange(n_k)
+    u = j & 31
+    block = 2 * (j >> 5) + ((u >> 3) & 1)
+    byte = 8 * (u >> 4) + (u & 7)
+    return blk_bytes[:, block, byte]
 
 
 def keep_mask(n: int, bh: int, p: float, seed: int, offset: int) -> np.ndarray:

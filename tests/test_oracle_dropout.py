@@ -1,43 +1,78 @@
-"""The dropout oracle against facts other than itself: numpy's own Philox4x64-10
-implementation (the generator and the element -> byte mapping written out through it),
-statistics of the mask, p = 0, an identity V that exposes P * Z, finite differences of the
-backward pass, unbiasedness over seeds, and planted mistakes that those pins catch."""
+"""The dropout oracle against facts other than itself: the ROCm random-number library's
+own Philox4x32-10 engine (the generator, and the element -> byte mapping written out
+through it), statistics of the mask, p = 0, an identity V that exposes P * Z, finite
+differences of the backward pass, unbiasedness over seeds, and planted mistakes that
+those pins catch."""
+import ctypes
+import os
+import subprocess
+
 import numpy as np
 import pytest
 
 import oracle
 from oracle import dropout as DR
 
-
-def _numpy_block(ctr, key):
-    """Philox4x64-10 block at `ctr` through numpy (its generator pre-increments)."""
-    c = [int(ctr[0]) - 1] + [int(x) for x in ctr[1:]]
-    bg = np.random.Philox(key=np.array(key, dtype=np.uint64), counter=np.array(c, dtype=np.uint64))
-    return [int(x) for x in bg.random_raw(4)]
+_HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def test_philox_matches_numpy():
+@pytest.fixture(scope="module")
+def rocrand_block(tmp_path_factory):
+    """Philox4x32-10 block through rocRAND's host-callable engine, built here with g++."""
+    out = str(tmp_path_factory.mktemp("philox") / "libphilox_ref.so")
+    subprocess.run(["g++", "-O1", "-fPIC", "-shared", "-D__HIP_PLATFORM_AMD__",
+                    "-I/opt/rocm/include", os.path.join(_HERE, "philox4x32_rocrand.cpp"),
+                    "-o", out], check=True, capture_output=True)
+    lib = ctypes.CDLL(out)
+    lib.philox4x32_rocrand.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int]
+
+    def block(ctr, key):
+        c = np.asarray(ctr, dtype=np.uint32).reshape(-1, 4).copy()
+        k = np.asarray(key, dtype=np.uint32).reshape(-1, 2).copy()
+        o = np.zeros_like(c)
+        lib.philox4x32_rocrand(c.ctypes.data, k.ctypes.data, o.ctypes.data, len(c))
+        return o
+    return block
+
+
+def test_philox_matches_rocrand(rocrand_block):
     rng = np.random.default_rng(1)
-    for _ in range(50):
-        ctr = [int(x) for x in rng.integers(1, 2**63, size=4, dtype=np.int64)]
-        ctr[1] |= int(rng.integers(0, 2)) << 63
-        key = [int(x) for x in rng.integers(0, 2**63, size=2, dtype=np.int64)]
-        key[0] |= 1 << 63
-        mine = [int(w) for w in DR.philox4x64(*(np.uint64(c) for c in ctr),
-                                              np.uint64(key[0]), np.uint64(key[1]))]
-        assert mine == _numpy_block(ctr, key)
+    n = 400
+    ctr = rng.integers(0, 2**32, size=(n, 4), dtype=np.uint64)
+    ctr[:, 1] >>= 2                       # the engine's offset is 4 (c0 + 2^32 c1) < 2^64
+    key = rng.integers(0, 2**32, size=(n, 2), dtype=np.uint64)
+    edge = np.array([[0, 0, 0, 0], [2**32 - 1, 2**30 - 1, 2**32 - 1, 2**32 - 1],
+                     [1, 0, 0, 0], [0, 0, 1, 0]], dtype=np.uint64)
+    ctr = np.concatenate([ctr, edge])
+    key = np.concatenate([key, np.array([[0, 0], [2**32 - 1, 2**32 - 1], [0, 1], [1, 0]],
+                                        dtype=np.uint64)])
+    mine = np.stack(DR.philox4x32(ctr[:, 0], ctr[:, 1], ctr[:, 2], ctr[:, 3], key[:, 0],
+                                  key[:, 1]), axis=-1)
+    assert np.array_equal(mine, rocrand_block(ctr, key))
 
 
-def test_byte_mapping_through_numpy():
-    """Byte of element (i, j) of head bh = byte j % 32 of the block at (i, j // 32, bh, 0)."""
+def _byte(rocrand_block, i, j, bh, seed, offset):
+    """The byte of element (i, j), spelled out one element at a time."""
+    g, u = j // 32, j % 32
+    blk = 2 * g + (u // 8) % 2
+    pos = 8 * (u // 16) + u % 8
+    words = rocrand_block([i, blk, bh, offset], [seed % 2**32, seed // 2**32])[0]
+    return int(words[pos // 4]) >> (8 * (pos % 4)) & 0xFF
+
+
+def test_byte_mapping_through_rocrand(rocrand_block):
     seed, offset, bh = 0xDEADBEEF12345678, 99, 5
     b = DR.random_bytes(40, 200, bh, seed, offset)
     rng = np.random.default_rng(2)
-    for _ in range(60):
-        i, j = int(rng.integers(1, 40)), int(rng.integers(0, 200))
-        words = _numpy_block([i, j // 32, bh, 0], [seed, offset])
-        raw = b"".join(w.to_bytes(8, "little") for w in words)
-        assert b[i, j] == raw[j % 32]
+    for _ in range(80):
+        i, j = int(rng.integers(0, 40)), int(rng.integers(0, 200))
+        assert b[i, j] == _byte(rocrand_block, i, j, bh, seed, offset)
+
+
+def test_key_range():
+    for seed, offset in ((-1, 0), (1 << 64, 0), (0, 1 << 32), (0, -1)):
+        with pytest.raises(ValueError):
+            DR.random_bytes(2, 2, 0, seed, offset)
 
 
 @pytest.mark.parametrize("p", [0.1, 0.25, 0.5])
@@ -141,12 +176,11 @@ def test_backward_mutants_are_caught(monkeypatch, kind):
         test_finite_differences()
 
 
-def test_transposed_mask_is_caught(monkeypatch):
+def test_transposed_mask_is_caught(monkeypatch, rocrand_block):
     orig = DR.random_bytes
     monkeypatch.setattr(DR, "random_bytes", lambda n_q, n_k, bh, s, o: orig(n_k, n_q, bh, s, o).T)
-    # the identity-V pin builds its own mask through the same function, so check against a
-    # block computed through numpy directly
+    # the identity-V pin builds its own mask through the same function, so check against
+    # bytes computed through rocRAND directly
     b = DR.random_bytes(40, 40, 1, 5, 6)
-    words = _numpy_block([3, 0, 1, 0], [5, 6])
-    raw = b"".join(w.to_bytes(8, "little") for w in words)
-    assert b[3, 17] != raw[17] or b[3, 9] != raw[9]
+    assert any(b[i, j] != _byte(rocrand_block, i, j, 1, 5, 6) for i, j in ((3, 17), (3, 9),
+                                                                          (30, 2)))
