@@ -12,7 +12,7 @@ kernel of the step timed with HIP events on the stream it runs on: fa_bwd is run
 three stages) and the CPU oracle's throughput on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--sweep] [--split-kv] [--sparse]
-                  [--no-cpu-baseline]
+                  [--dropout] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -145,6 +145,10 @@ def main():
     ap.add_argument("--sparse", action="store_true",
                     help="also print block-sparse lines: forward and backward time against the "
                          "fraction of 128x128 blocks evaluated (supplementary)")
+    ap.add_argument("--dropout", action="store_true",
+                    help="also print dropout lines: forward and backward with the mask drawn "
+                         "and regenerated on chip, against the kernels without dropout "
+                         "(supplementary)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy a MIB-MiB buffer once (a plain copy kernel of known size, "
@@ -234,6 +238,8 @@ def main():
         split_kv(fa, torch, workloads)
     if args.sparse:
         sparse(fa, torch, workloads)
+    if args.dropout:
+        dropout(fa, torch, workloads)
 
 
 def sweep(fa, torch, workloads):
@@ -341,6 +347,37 @@ def sparse(fa, torch, workloads):
                 "fwd_time_frac": round(t_f / t_fd, 4), "bwd_time_frac": round(t_b / t_bd, 4),
                 "sparse_fwd_tflops": round(frac * w.fwd_flops() / t_f / 1e9, 2),
                 "sparse_bwd_tflops": round(frac * w.bwd_flops() / t_b / 1e9, 2)}), flush=True)
+
+
+
+def dropout(fa, torch, workloads):
+    """Supplementary lines: forward and backward with dropout (Philox blocks drawn in the
+    forward kernel and drawn again in both backward kernels) next to the same kernels
+    without dropout, on the same inputs. FLOPs are the dense nominal counts."""
+    for B, H, N, d, causal in [(2, 16, 4096, 128, True), (1, 16, 8192, 64, False)]:
+        w, inp = workloads.custom(B, H, N, d, "bf16", causal, seed=0)
+        dev = {n: inp[n].cuda() for n in ("q", "k", "v", "dout")}
+        ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8,
+                         device="cuda")
+        o, lse = fa.fa_fwd(dev["q"], dev["k"], dev["v"], causal=causal, scale=w.scale)
+        t_fd = _time(torch, lambda: fa.fa_fwd(dev["q"], dev["k"], dev["v"], causal=causal,
+                                              scale=w.scale, out=o, lse=lse))
+        t_bd = _time(torch, lambda: fa.fa_bwd(dev["q"], dev["k"], dev["v"], o, dev["dout"], lse,
+                                              causal=causal, scale=w.scale, workspace=ws))
+        for p in (0.1,):
+            kw = dict(p=p, seed=1234, offset=0, causal=causal, scale=w.scale)
+            od, ld = fa.fa_fwd_dropout(dev["q"], dev["k"], dev["v"], **kw)
+            t_f = _time(torch, lambda: fa.fa_fwd_dropout(dev["q"], dev["k"], dev["v"], out=od,
+                                                         lse=ld, **kw))
+            t_b = _time(torch, lambda: fa.fa_bwd_dropout(dev["q"], dev["k"], dev["v"], od,
+                                                         dev["dout"], ld, workspace=ws, **kw))
+            print(json.dumps({
+                "dropout": True, "p": p, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                "dense_fwd_ms": round(t_fd, 4), "dense_bwd_ms": round(t_bd, 4),
+                "dropout_fwd_ms": round(t_f, 4), "dropout_bwd_ms": round(t_b, 4),
+                "fwd_time_ratio": round(t_f / t_fd, 4), "bwd_time_ratio": round(t_b / t_bd, 4),
+                "dropout_fwd_tflops": round(w.fwd_flops() / t_f / 1e9, 2),
+                "dropout_bwd_tflops": round(w.bwd_flops() / t_b / 1e9, 2)}), flush=True)
 
 
 if __name__ == "__main__":

@@ -199,12 +199,13 @@ FA_API int fa_bwd_stage(int stage, const void* q, const void* k, const void* v,
  * (summary of arXiv 2205.14135): Key ideas (kernel fusion) fuses dropout into the one
  * attention kernel, and the FAQ on recomputation has the backward pass regenerate the
  * dropout mask on chip from the stored state of the random generator instead of reading
- * it from HBM. The pages name no generator; this library uses Philox4x64-10 (Salmon,
- * Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC11), keyed by
- * (seed, offset): the random byte of element (batch b, head h, query i, key j) is byte
- * j % 32, little-endian, of the four 64-bit words the generator returns for the counter
- * (i, j / 32, b*H + h, 0). With t = round(256 p) (at most 255) an element is kept iff
- * its byte >= t, and kept probabilities are scaled by 256 / (256 - t):
+ * it from HBM. The pages name no generator; this library uses Philox4x32-10 (Salmon,
+ * Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC11) under the key
+ * (seed mod 2^32, seed >> 32). Keys fall in groups of 32: for element (batch b, head h,
+ * query i, key j = 32 g + u) the random byte is byte 8*(u/16) + u%8 (little-endian over
+ * the four 32-bit output words) of the block at counter (i, 2g + (u/8)%2, b*H + h,
+ * offset). With t = round(256 p) (at most 255) an element is kept iff its byte >= t, and
+ * kept probabilities are scaled by 256 / (256 - t):
  *   o = (P * Z * 256/(256 - t)) v, lse = log-sum-exp of the undropped scaled scores.
  * fa_bwd_dropout computes the gradients of that o with the same mask (same p, seed and
  * offset; o and lse from fa_fwd_dropout). p must lie in [0, 1) (else FA_EINVAL); p = 0
@@ -215,13 +216,13 @@ FA_API int fa_bwd_stage(int stage, const void* q, const void* k, const void* v,
  */
 FA_API int fa_fwd_dropout(const void* q, const void* k, const void* v, float* o, float* lse,
                    int B, int H, int N, int d, float scale, int causal, int dtype,
-                   const int32_t* kv_len, float p, uint64_t seed, uint64_t offset,
+                   const int32_t* kv_len, float p, uint64_t seed, uint32_t offset,
                    void* stream);
 
 FA_API int fa_bwd_dropout(const void* q, const void* k, const void* v, const float* o,
                    const void* dout, const float* lse, float* dq, float* dk, float* dv,
                    int B, int H, int N, int d, float scale, int causal, int dtype,
-                   const int32_t* kv_len, float p, uint64_t seed, uint64_t offset,
+                   const int32_t* kv_len, float p, uint64_t seed, uint32_t offset,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */

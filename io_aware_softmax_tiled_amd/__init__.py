@@ -89,11 +89,12 @@ def load_library() -> ctypes.CDLL:
                                   i32, i32, vp, vp, vp, sz, vp]
     lib.fa_bwd_sparse.restype = i32
     u64 = ctypes.c_uint64
+    u32 = ctypes.c_uint32
     lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, i32, vp,
-                                   f32, u64, u64, vp]
+                                   f32, u64, u32, vp]
     lib.fa_fwd_dropout.restype = i32
     lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
-                                   i32, i32, vp, f32, u64, u64, vp, sz, vp]
+                                   i32, i32, vp, f32, u64, u32, vp, sz, vp]
     lib.fa_bwd_dropout.restype = i32
     lib.fa_status_str.argtypes = [i32]
     lib.fa_status_str.restype = ctypes.c_char_p
@@ -327,15 +328,16 @@ def fa_bwd_sparse(q, k, v, o, dout, lse, block_mask, *, causal=False, scale=None
 
 def _key(seed, offset):
     seed, offset = int(seed), int(offset)
-    if not (0 <= seed < 1 << 64 and 0 <= offset < 1 << 64):
-        raise ValueError("seed and offset are unsigned 64-bit integers")
+    if not (0 <= seed < 1 << 64 and 0 <= offset < 1 << 32):
+        raise ValueError("seed is an unsigned 64-bit and offset an unsigned 32-bit integer")
     return seed, offset
 
 
 def fa_fwd_dropout(q, k, v, *, p, seed, offset=0, causal=False, scale=None, kv_len=None,
                    out=None, lse=None, stream=None):
-    """Forward with dropout p on the probabilities, mask drawn from Philox4x64-10 keyed by
-    (seed, offset): returns (o, lse), lse that of the undropped scores."""
+    """Forward with dropout p on the probabilities, mask drawn from Philox4x32-10 keyed by
+    seed (64-bit) with offset (32-bit) in its counters: returns (o, lse), lse that of the
+    undropped scores."""
     seed, offset = _key(seed, offset)
     B, H, N, d = _shape(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)

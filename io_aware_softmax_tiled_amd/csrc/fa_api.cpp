@@ -101,7 +101,8 @@ int check_sparse(int N, int dtype, const uint8_t* block_mask) {
 // Dropout of the probabilities: byte threshold t (-1: none) and the generator key.
 struct Drop {
   int t = -1;
-  uint64_t seed = 0, offset = 0;
+  uint64_t seed = 0;
+  uint32_t offset = 0;
 };
 
 // t = round(256 p), keep iff the element's random byte >= t.
@@ -175,7 +176,7 @@ int fa_fwd_sparse(const void* q, const void* k, const void* v, float* o, float* 
 
 int fa_fwd_dropout(const void* q, const void* k, const void* v, float* o, float* lse, int B,
                    int H, int N, int d, float scale, int causal, int dtype,
-                   const int32_t* kv_len, float p, uint64_t seed, uint64_t offset,
+                   const int32_t* kv_len, float p, uint64_t seed, uint32_t offset,
                    void* stream) {
   clear_error();
   int st = check_common(B, H, N, d, scale, dtype);
@@ -373,7 +374,7 @@ int fa_bwd_sparse(const void* q, const void* k, const void* v, const float* o,
 int fa_bwd_dropout(const void* q, const void* k, const void* v, const float* o,
                    const void* dout, const float* lse, float* dq, float* dk, float* dv, int B,
                    int H, int N, int d, float scale, int causal, int dtype,
-                   const int32_t* kv_len, float p, uint64_t seed, uint64_t offset,
+                   const int32_t* kv_len, float p, uint64_t seed, uint32_t offset,
                    void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
   int st = check_common(B, H, N, d, scale, dtype);

@@ -88,9 +88,10 @@ constexpr int kBQ = 64;   // queries per tile (two 32-query halves)
 constexpr int kSparseBlock = 128;
 constexpr int kSparseMaxBlocks = 2048;  // blocks per row/column of the mask (N <= 2^18)
 
-// kDropout: the probabilities carry the forward pass's dropout mask Z (regenerated here
-// from the same Philox4x64-10 blocks: element (i, j) of head bh is byte j % 32 of the
-// block at counter (i, j / 32, bh, 0), key (seed, offset); kept iff >= drop_t):
+// kDropout: the probabilities carry the forward pass's dropout mask Z, regenerated here
+// from the same Philox4x32-10 blocks (element (i, 32 g + u) of head bh: byte
+// 8 (u / 16) + u % 8 of the block at counter (i, 2 g + (u / 8) % 2, bh, offset); kept
+// iff >= drop_t):
 // dV = (P Z / keep)^T dO, dP = (Z / keep) (dO V^T), dS = P (dP - D).
 template <typename T, int D, bool kSparse, bool kDropout>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
@@ -99,8 +100,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const float* __restrict__ LSE, const float* __restrict__ delta, float* __restrict__ dK,
     float* __restrict__ dV, int BH, int H, int N, float scale, float sl2, int causal,
     const int* __restrict__ kv_len, int n_kblk, int heads_per_xcd,
-    const uint8_t* __restrict__ bmask, int n_sb, uint64_t seed, uint64_t offset, int drop_t,
-    float keep_scale) {
+    const uint8_t* __restrict__ bmask, int n_sb, uint32_t seed_lo, uint32_t seed_hi,
+    uint32_t offset, int drop_t, float keep_scale) {
   constexpr int kKC = D / 16;
   constexpr int kDB = D / 32;
   constexpr int kCPR = D / 8;                        // 16-byte chunks per row
@@ -371,14 +372,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bool need_mask =
         (causal && kw0 + 31 > q0) || (q0 + kBQ > N) || (kw0 + 32 > kv_lim);
     if (kDropout && active) {
-      // lane l generates the 32 bytes of (query q0 + l, this wave's 32 keys) and stores
-      // them for the wave; each lane then reads the bytes of its own key
-      const Philox4x64 ph = philox4x64((uint64_t)(q0 + lane), (uint64_t)(kw0 >> 5),
-                                       (uint64_t)bh, 0ull, seed, offset);
-      lds_write16(zw + lane * 32, u32x4{(uint32_t)ph.w[0], (uint32_t)(ph.w[0] >> 32),
-                                        (uint32_t)ph.w[1], (uint32_t)(ph.w[1] >> 32)});
-      lds_write16(zw + lane * 32 + 16, u32x4{(uint32_t)ph.w[2], (uint32_t)(ph.w[2] >> 32),
-                                             (uint32_t)ph.w[3], (uint32_t)(ph.w[3] >> 32)});
+      // lane l draws the two blocks of (query q0 + l, this wave's 32 keys) and stores
+      // the 32 bytes in key order for the wave (keys 0-7: bytes 0-7 of the first block,
+      // 8-15: of the second, 16-23: bytes 8-15 of the first, 24-31: of the second);
+      // each lane then reads the bytes of its own key
+      const uint32_t qg = (uint32_t)(q0 + lane), kb = (uint32_t)(2 * (kw0 >> 5));
+      const Philox4x32 b0 = philox4x32(qg, kb, (uint32_t)bh, offset, seed_lo, seed_hi);
+      const Philox4x32 b1 = philox4x32(qg, kb + 1, (uint32_t)bh, offset, seed_lo, seed_hi);
+      lds_write16(zw + lane * 32, u32x4{b0.w[0], b0.w[1], b1.w[0], b1.w[1]});
+      lds_write16(zw + lane * 32 + 16, u32x4{b0.w[2], b0.w[3], b1.w[2], b1.w[3]});
     }
     if (active) {
       f32x16 s0, dp0, s1, dp1;
@@ -460,8 +462,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const float* __restrict__ LSE, const float* __restrict__ delta, float* __restrict__ dQ,
     int BH, int H, int N, float scale, float sl2, int causal,
     const int* __restrict__ kv_len, int n_mblk, int heads_per_xcd,
-    const uint8_t* __restrict__ bmask, int n_sb, uint64_t seed, uint64_t offset, int drop_t,
-    float keep_scale) {
+    const uint8_t* __restrict__ bmask, int n_sb, uint32_t seed_lo, uint32_t seed_hi,
+    uint32_t offset, int drop_t, float keep_scale) {
   constexpr int kKC = D / 16;
   constexpr int kDB = D / 32;
   constexpr int kCPR = D / 8;
@@ -603,14 +605,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         }
       }
       uint32_t dsk[8];
-      uint64_t rnd[2] = {0, 0};
+      uint32_t rnd[4] = {0, 0, 0, 0};
       if constexpr (kDropout) {
-        // registers 8c .. 8c+7 hold keys n0 + 32 sub + 16c + 8 hh + 0..7: the bytes of
-        // word 2c + hh of the sub-block's Philox block
-        const Philox4x64 ph = philox4x64((uint64_t)qrow, (uint64_t)((n0 + 32 * sub) >> 5),
-                                         (uint64_t)bh, 0ull, seed, offset);
-        rnd[0] = hh ? ph.w[1] : ph.w[0];
-        rnd[1] = hh ? ph.w[3] : ph.w[2];
+        // register r holds key n0 + 32 sub + 16 (r / 8) + 8 hh + r % 8, whose byte is
+        // byte r of the block at counter (query, 2 (sub-block) + hh, head, offset)
+        const Philox4x32 ph = philox4x32((uint32_t)qrow,
+                                         (uint32_t)(2 * ((n0 + 32 * sub) >> 5) + hh),
+                                         (uint32_t)bh, offset, seed_lo, seed_hi);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) rnd[w] = ph.w[w];
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -618,7 +621,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         const float p1 = exp2_fast(fmaf(st[2 * i + 1], sl2, -lse2));
         float dp0 = dpt[2 * i], dp1 = dpt[2 * i + 1];
         if constexpr (kDropout) {
-          const uint64_t wv = rnd[i >> 2] >> (16 * (i & 3));
+          const uint32_t wv = rnd[i >> 1] >> (16 * (i & 1));
           dp0 = (int)(wv & 0xff) >= drop_t ? dp0 * keep_scale : 0.f;
           dp1 = (int)((wv >> 8) & 0xff) >= drop_t ? dp1 * keep_scale : 0.f;
         }
@@ -688,6 +691,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages) {
   const int n_sb = (a.N + kSparseBlock - 1) / kSparseBlock;
   const bool dropout = a.drop_t >= 0;
   const float keep_scale = dropout ? 256.0f / (float)(256 - a.drop_t) : 1.0f;
+  const uint32_t seed_lo = (uint32_t)a.seed, seed_hi = (uint32_t)(a.seed >> 32);
 #define FA_BWD_LAUNCH2(TAG, DIM, SP, DR)                                                     \
   do {                                                                                       \
     if (stages & 1)                                                                          \
@@ -697,12 +701,13 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages) {
       hipLaunchKernelGGL((bwd_dkdv_kernel<TAG, DIM, SP, DR>), dim3(8 * hpx * n_kblk),        \
                          dim3(kThreads), 0, stream, q16, k16, v16, dO16, a.lse, a.delta,     \
                          a.dk, a.dv, BH, a.H, a.N, a.scale, sl2, a.causal, a.kv_len, n_kblk, \
-                         hpx, a.block_mask, n_sb, a.seed, a.offset, a.drop_t, keep_scale);   \
+                         hpx, a.block_mask, n_sb, seed_lo, seed_hi, a.offset, a.drop_t,      \
+                         keep_scale);                                                        \
     if (stages & 4)                                                                          \
       hipLaunchKernelGGL((bwd_dq_kernel<TAG, DIM, SP, DR>), dim3(8 * hpx * n_mblk),          \
                          dim3(kThreads), 0, stream, q16, k16, v16, dO16, a.lse, a.delta,     \
                          a.dq, BH, a.H, a.N, a.scale, sl2, a.causal, a.kv_len, n_mblk, hpx,  \
-                         a.block_mask, n_sb, a.seed, a.offset, a.drop_t, keep_scale);        \
+                         a.block_mask, n_sb, seed_lo, seed_hi, a.offset, a.drop_t, keep_scale); \
   } while (0)
 #define FA_BWD_LAUNCH(TAG, DIM)                                          \
   do {                                                                   \

@@ -134,32 +134,31 @@ __device__ inline u32x2 lds_read_tr16(const FA_LDS uint8_t* p) {
 // memory clobber keeps the compiler from moving memory accesses across it.
 __device__ inline void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Philox4x64-10 counter-based generator (Salmon, Moraes, Dror, Shaw, "Parallel random
-// numbers: as easy as 1, 2, 3", SC11): ten rounds over a 4 x 64-bit counter with a
-// 2 x 64-bit key; each round multiplies counter words 0 and 2 by fixed constants, keeps
-// both 64-bit halves of the products and mixes them with words 1 and 3 and the round key;
-// the key advances by fixed Weyl increments between rounds. The dropout mask is a pure
-// function of (counter, key), so the backward pass regenerates it on chip.
-struct Philox4x64 {
-  uint64_t w[4];
+// Philox4x32-10 counter-based generator (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC11): ten rounds over a 4 x 32-bit counter with a
+// 2 x 32-bit key; each round multiplies counter words 0 and 2 by fixed constants, keeps
+// both 32-bit halves of the 64-bit products (one v_mad_u64_u32 each) and mixes them with
+// words 1 and 3 and the round key; the key advances by fixed Weyl increments between
+// rounds. The dropout mask is a pure function of (counter, key), so the backward pass
+// regenerates it on chip.
+struct Philox4x32 {
+  uint32_t w[4];
 };
-__device__ inline Philox4x64 philox4x64(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
-                                        uint64_t k0, uint64_t k1) {
-  constexpr uint64_t kM0 = 0xD2E7470EE14C6C93ull, kM1 = 0xCA5A826395121157ull;
-  constexpr uint64_t kW0 = 0x9E3779B97F4A7C15ull, kW1 = 0xBB67AE8584CAA73Bull;
+__device__ inline Philox4x32 philox4x32(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                        uint32_t k0, uint32_t k1) {
+  constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
+  constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    if (r) {
-      k0 += kW0;
-      k1 += kW1;
-    }
-    const uint64_t hi0 = __umul64hi(kM0, c0), lo0 = kM0 * c0;
-    const uint64_t hi1 = __umul64hi(kM1, c2), lo1 = kM1 * c2;
-    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    const uint64_t p0 = (uint64_t)kM0 * c0, p1 = (uint64_t)kM1 * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
     c0 = n0;
-    c1 = lo1;
+    c1 = (uint32_t)p1;
     c2 = n2;
-    c3 = lo0;
+    c3 = (uint32_t)p0;
+    k0 += kW0;
+    k1 += kW1;
   }
   return {{c0, c1, c2, c3}};
 }

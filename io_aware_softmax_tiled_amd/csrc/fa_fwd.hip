@@ -70,9 +70,9 @@ constexpr int kThreads = 256;
 // In both modes a row that sees no key gets O = 0 and LSE = -inf.
 // kMode 3, dropout: the normalised probabilities are multiplied by Z / keep, Z_ij = 1
 // iff random byte (i, j) >= drop_t, keep = (256 - drop_t) / 256 (keep_scale = 1/keep);
-// byte (i, j) of head bh is byte j % 32 of the Philox4x64-10 block at counter
-// (i, j / 32, bh, 0) and key (seed, offset). The statistics (and LSE) are those of the
-// undropped scores.
+// byte (i, j) of head bh, with j = 32 g + u, is byte 8 (u / 16) + u % 8 of the
+// Philox4x32-10 block at counter (i, 2 g + (u / 8) % 2, bh, offset) under the key
+// (seed_lo, seed_hi). The statistics (and LSE) are those of the undropped scores.
 constexpr int kSparseBlock = 128;
 constexpr int kSparseMaxBlocks = 2048;  // key blocks per row of the mask (N <= 2^18)
 
@@ -83,7 +83,8 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
     int BH, int H, int N, float scale, float sl2, int causal,
     const int* __restrict__ kv_len, int n_mblk, int heads_per_xcd, int split_len,
     int per_split, size_t o_stride, size_t lse_stride, const uint8_t* __restrict__ bmask,
-    int n_sb, uint64_t seed, uint64_t offset, int drop_t, float keep_scale) {
+    int n_sb, uint32_t seed_lo, uint32_t seed_hi, uint32_t offset, int drop_t,
+    float keep_scale) {
   constexpr bool kPartial = kMode == 1;
   constexpr bool kSparse = kMode == 2;
   constexpr bool kDropout = kMode == 3;
@@ -305,15 +306,15 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   // P = exp2(s*scale*log2e - m_ref*scale*log2e), rounded to fp16, and its row sum;
   // with dropout the product takes P * Z (the scale 1/keep is applied at the end) while
   // the row sum takes P. Sub-block sb: keys 32*sb .. 32*sb+31; this lane's register r
-  // holds key 32*sb + 16*(r/8) + 8*hh + r%8, i.e. byte r%8 of word 2*(r/8) + hh of the
-  // sub-block's Philox block.
+  // holds key 32*sb + 16*(r/8) + 8*hh + r%8, whose random byte is byte r of the Philox
+  // block at counter (query, 2*sb + hh, head, offset): one block per lane and sub-block.
   auto expo = [&](const f32x16& s, uint32_t (&pk)[8], int sb) {
-    uint64_t rnd[2] = {0, 0};
+    uint32_t rnd[4] = {0, 0, 0, 0};
     if constexpr (kDropout) {
-      const Philox4x64 ph = philox4x64((uint64_t)qrow, (uint64_t)sb, (uint64_t)pos.bh, 0ull,
-                                       seed, offset);
-      rnd[0] = hh ? ph.w[1] : ph.w[0];
-      rnd[1] = hh ? ph.w[3] : ph.w[2];
+      const Philox4x32 ph = philox4x32((uint32_t)qrow, (uint32_t)(2 * sb + hh),
+                                       (uint32_t)pos.bh, offset, seed_lo, seed_hi);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) rnd[w] = ph.w[w];
     }
     // (a row that has seen no visible key yet -- possible in a split or a sparse
     // pattern -- keeps
@@ -326,8 +327,8 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
       pk[i] = Mfma<F16>::pack(p0, p1);
       lsum = Mfma<F16>::dot_ones(pk[i], lsum);
       if constexpr (kDropout) {
-        // registers 2i, 2i+1: bytes (2i)%8 and (2i+1)%8 of word i/4
-        const uint64_t wv = rnd[i >> 2] >> (16 * (i & 3));
+        // registers 2i, 2i+1: bytes 2i and 2i+1, in word i/2
+        const uint32_t wv = rnd[i >> 1] >> (16 * (i & 1));
         const bool keep0 = (int)(wv & 0xff) >= drop_t;
         const bool keep1 = (int)((wv >> 8) & 0xff) >= drop_t;
         pk[i] = Mfma<F16>::pack(keep0 ? p0 : 0.f, keep1 ? p1 : 0.f);
@@ -685,7 +686,8 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
                      dim3(WV * 64), 0, stream, q16, k16, v16, a.o, a.lse, BH, a.H, a.N,     \
                      a.scale, sl2, a.causal, a.kv_len, g.n_mblk, g.heads_per_xcd,           \
                      a.split_len, g.blocks, o_stride, lse_stride, a.block_mask, n_sb,      \
-                     a.seed, a.offset, a.drop_t, keep_scale)
+                     (uint32_t)a.seed, (uint32_t)(a.seed >> 32), a.offset, a.drop_t,       \
+                     keep_scale)
   // head_dim 128 always runs 8 waves (its LDS use allows one workgroup per CU)
 #define FA_LAUNCH16(TAG, DIM, MODE)                                 \
   do {                                                              \

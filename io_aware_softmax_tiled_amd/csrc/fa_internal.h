@@ -28,9 +28,10 @@ struct FwdArgs {
   // evaluated; nullptr for dense attention
   const uint8_t* block_mask = nullptr;
   // dropout: byte threshold t in [0, 255] (keep iff byte >= t), -1 for none; the mask
-  // generator's key is (seed, offset)
+  // generator is keyed by seed, its counters carry offset
   int drop_t = -1;
-  uint64_t seed = 0, offset = 0;
+  uint64_t seed = 0;
+  uint32_t offset = 0;
 };
 
 struct FwdGrid {
@@ -60,7 +61,8 @@ struct BwdArgs {
   float* delta;  // workspace: D_i = rowsum(dO * O), [B,H,N]
   const uint8_t* block_mask = nullptr;  // block-sparse mask as in FwdArgs, or nullptr
   int drop_t = -1;                      // dropout as in FwdArgs
-  uint64_t seed = 0, offset = 0;
+  uint64_t seed = 0;
+  uint32_t offset = 0;
 };
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d);

@@ -272,7 +272,7 @@ def test_dropout_fwd_rejects_before_launch(lib, kw, code):
 
 
 def test_dropout_empty_is_noop(lib):
-    assert _dfwd(lib, N=0, seed=(1 << 64) - 1, offset=(1 << 64) - 1) == FA_OK
+    assert _dfwd(lib, N=0, seed=(1 << 64) - 1, offset=(1 << 32) - 1) == FA_OK
 
 
 def test_dropout_bwd_rejects_before_launch(lib):
@@ -290,6 +290,6 @@ def test_dropout_bwd_rejects_before_launch(lib):
 def test_dropout_binding_checks_key():
     import torch
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
-    for seed, offset in ((-1, 0), (0, 1 << 64)):
+    for seed, offset in ((-1, 0), (1 << 64, 0), (0, 1 << 32), (0, -1)):
         with pytest.raises(ValueError):
             fa.fa_fwd_dropout(q, q, q, p=0.1, seed=seed, offset=offset)

@@ -1,6 +1,6 @@
 """Dropout parity on the GPU: fa_fwd_dropout / fa_bwd_dropout (HIP, through the C ABI)
 against the fp64 oracle's attention with dropout, whose mask comes from the oracle's own
-Philox4x64-10. Besides the tolerance tests on random inputs, three tests read the mask
+Philox4x32-10. Besides the tolerance tests on random inputs, three tests read the mask
 the kernels used back out of O, dV and dQ with one-hot inputs and compare it bit for bit
 with the oracle's mask."""
 import numpy as np
