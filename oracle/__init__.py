@@ -11,8 +11,9 @@ attention         The plain definition: S = scale*Q K^T with the causal and key-
                   backward. Materialises S and P (per head, in row blocks).
 page_algorithms   The softmax / attention recurrences the pages derive (3-pass safe
                   softmax, 2-pass online softmax, 2-pass and 1-pass FlashAttention rows,
-                  the tiled recurrence, the Br x Bc block update, the statistics merge),
-                  written as scalar float64 loops. They cross-check the definition.
+                  the tiled recurrence, the Br x Bc block update, the statistics merge,
+                  and the issue thread's deferred P V variant), written as scalar
+                  float64 loops. They cross-check the definition.
 split             Split-KV: attention over contiguous key ranges (normalised partial
                   outputs with their LSE, empty rows O = 0, LSE = -inf) and the merge
                   of partials by the incremental softmax tracking rule.

@@ -219,3 +219,57 @@ def attention_blocks(Q, K, V, Br, Bc, scale=1.0, allowed=None):
         O[i0:i0 + len(rows)] = Oi
         lse[i0:i0 + len(rows)] = [mi[r] + math.log(li[r]) for r in range(len(rows))]
     return O, lse
+
+
+# ---- "Fewer matrix multiplications, same results" (flash-attention issue thread):
+# ---- the deferred P V variant ------------------------------------------------------
+
+def attention_deferred_pv(Q, K, V, block, scale=1.0, allowed=None):
+    """The thread's variant, for one head: per query block, the numerator blocks f_j of
+    the whole key row are kept and only one product with V is formed at the end.
+
+    For query block i and key blocks j = 0, 1, ...: S_ij = scale * Q_i K_j^T (masked
+    entries -inf); m_loc = rowmax(S_ij); f_j = exp(S_ij - m_loc); l_loc = rowsum(f_j).
+    For j = 0 the state is (m, l) = (m_loc, l_loc). Otherwise m_new = max(m, m_loc),
+    l_new = e^{m - m_new} l + e^{m_loc - m_new} l_loc, every earlier block f_k (k < j)
+    is multiplied by e^{m - m_new}, f_j by e^{m_loc - m_new}, and (m, l) <- (m_new,
+    l_new). At the end O_i = (f / l) V with f = [f_0 ... f_last]. The thread writes the
+    blocks as square (query block = key block) and adds a small constant to l_loc; here
+    the key blocks are `block` wide, the last one ragged, and nothing is added.
+    Returns (O [N,d], LSE [N]) with LSE = m + ln l.
+    """
+    Q, K, V = (np.asarray(a, dtype=np.float64) for a in (Q, K, V))
+    n, nk, dv = Q.shape[0], K.shape[0], V.shape[1]
+    O = np.zeros((n, dv))
+    lse = np.zeros(n)
+    for i0 in range(0, n, block):
+        rows = list(range(i0, min(n, i0 + block)))
+        f_blocks = []
+        m = [NEG_INF] * len(rows)
+        l = [0.0] * len(rows)
+        for jb, j0 in enumerate(range(0, nk, block)):
+            cols = list(range(j0, min(nk, j0 + block)))
+            S = scale * (Q[rows[0]:rows[-1] + 1] @ K[j0:cols[-1] + 1].T)
+            for r, row in enumerate(rows):
+                for c, col in enumerate(cols):
+                    if allowed is not None and not allowed[row][col]:
+                        S[r, c] = NEG_INF
+            f = np.zeros_like(S)
+            for r in range(len(rows)):
+                m_loc = max(S[r, c] for c in range(len(cols)))
+                f[r] = [_w(S[r, c], m_loc) for c in range(len(cols))]
+                l_loc = float(sum(f[r]))
+                if jb == 0:
+                    m[r], l[r] = m_loc, l_loc
+                    continue
+                m_new = max(m[r], m_loc)
+                a_old, a_loc = _w(m[r], m_new), _w(m_loc, m_new)
+                for fk in f_blocks:
+                    fk[r] *= a_old
+                f[r] *= a_loc
+                m[r], l[r] = m_new, a_old * l[r] + a_loc * l_loc
+            f_blocks.append(f)
+        F = np.concatenate(f_blocks, axis=1)
+        O[rows[0]:rows[-1] + 1] = (F / np.array(l)[:, None]) @ V
+        lse[rows[0]:rows[-1] + 1] = [m[r] + math.log(l[r]) for r in range(len(rows))]
+    return O, lse

@@ -104,3 +104,51 @@ def test_flashatt_spec_is_attention_with_unit_head_dim():
     # and against scipy's softmax written out
     ref = [(scipy.special.softmax(qi * k) * v).sum() for qi in q]
     assert np.max(np.abs(z - np.array(ref))) < 1e-13
+
+
+def _rising_case(N=23, d=3, step=2.0):
+    """Scores that rise along the keys, so every key block raises the running maximum
+    and every earlier numerator block must be rescaled."""
+    rng = np.random.default_rng(8)
+    q = np.zeros((N, d))
+    q[:, 0] = 1.0 + 0.1 * rng.random(N)
+    k = 0.1 * rng.standard_normal((N, d))
+    k[:, 0] = step * np.arange(N)
+    v = rng.standard_normal((N, d))
+    return q, k, v
+
+
+def test_deferred_pv_matches_definition():
+    cases = list(_row_cases())
+    q, k, v = _rising_case()
+    cases += [(23, 3, False, None, q, k, v), (23, 3, True, None, q, k, v),
+              (23, 3, False, 17, q, k, v)]
+    for N, d, causal, kvb, q, k, v in cases:
+        o_ref, l_ref = oracle.head_forward(q, k, v, 0.55, causal, kvb)
+        vis = _vis(N, causal, kvb)
+        for blk in sorted({1, 3, 4, 5, N}):
+            o, l = pa.attention_deferred_pv(q, k, v, blk, 0.55, vis)
+            assert np.max(np.abs(o - o_ref)) < 1e-12, (N, blk)
+            assert np.max(np.abs(l - l_ref)) < 1e-12 * max(1, np.abs(l_ref).max()), (N, blk)
+
+
+def test_deferred_pv_needs_its_rescale():
+    """The rising case separates the rule from a variant that leaves the earlier blocks
+    unscaled (which stays exact only while the maximum never moves)."""
+    q, k, v = _rising_case()
+    vis = _vis(23, False, None)
+    o_ref, _ = oracle.head_forward(q, k, v, 0.55, False, None)
+    # the variant, by hand: numerators kept relative to their own block maximum
+    blk = 4
+    F, m_all = [], []
+    for j0 in range(0, 23, blk):
+        S = 0.55 * (q @ k[j0:j0 + blk].T)
+        m_loc = S.max(axis=1)
+        F.append(np.exp(S - m_loc[:, None]))
+        m_all.append(m_loc)
+    m_fin = np.max(np.stack(m_all, 1), axis=1)
+    l_wrong = sum(f.sum(1) * np.exp(m - m_fin) for f, m in zip(F, m_all))
+    o_wrong = (np.concatenate(F, 1) / l_wrong[:, None]) @ v
+    assert np.max(np.abs(o_wrong - o_ref)) > 1e-3
+    o, _ = pa.attention_deferred_pv(q, k, v, blk, 0.55, vis)
+    assert np.max(np.abs(o - o_ref)) < 1e-12
