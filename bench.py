@@ -12,7 +12,7 @@ kernel of the step timed with HIP events on the stream it runs on: fa_bwd is run
 three stages) and the CPU oracle's throughput on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--sweep] [--split-kv] [--sparse]
-                  [--dropout] [--no-cpu-baseline]
+                  [--dropout] [--deferred] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -149,6 +149,10 @@ def main():
                     help="also print dropout lines: forward and backward with the mask drawn "
                          "and regenerated on chip, against the kernels without dropout "
                          "(supplementary)")
+    ap.add_argument("--deferred", action="store_true",
+                    help="also print deferred-PV lines: the forward that keeps a query "
+                         "block's whole numerator row on chip and multiplies by V once, "
+                         "against the single-pass forward (supplementary)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy a MIB-MiB buffer once (a plain copy kernel of known size, "
@@ -240,6 +244,8 @@ def main():
         sparse(fa, torch, workloads)
     if args.dropout:
         dropout(fa, torch, workloads)
+    if args.deferred:
+        deferred(fa, torch, workloads)
 
 
 def sweep(fa, torch, workloads):
@@ -378,6 +384,34 @@ def dropout(fa, torch, workloads):
                 "fwd_time_ratio": round(t_f / t_fd, 4), "bwd_time_ratio": round(t_b / t_bd, 4),
                 "dropout_fwd_tflops": round(w.fwd_flops() / t_f / 1e9, 2),
                 "dropout_bwd_tflops": round(w.bwd_flops() / t_b / 1e9, 2)}), flush=True)
+
+
+
+def deferred(fa, torch, workloads):
+    """Supplementary lines: the deferred-PV forward (numerator row kept on chip, one
+    product with V) against the single-pass forward, on the BERT-large key-padding
+    workload and on short sequences at 8K tokens. FLOPs are the nominal counts."""
+    shapes = [(8, 16, 512, 64, False, (256, 512))]
+    for N in (128, 256, 512):
+        for d in (64, 128):
+            for causal in (False, True):
+                shapes.append((8192 // N, 2048 // d, N, d, causal, None))
+    for B, H, N, d, causal, kv in shapes:
+        w, inp = workloads.custom(B, H, N, d, "bf16", causal, kv_range=kv, seed=0,
+                                  with_dout=False)
+        dev = {n: inp[n].cuda() for n in ("q", "k", "v")}
+        kvl = None if inp["kv_len"] is None else inp["kv_len"].cuda()
+        o = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        kw = dict(causal=causal, scale=w.scale, kv_len=kvl, out=o, lse=lse)
+        t_one = _time(torch, lambda: fa.fa_fwd(dev["q"], dev["k"], dev["v"], **kw))
+        t_def = _time(torch, lambda: fa.fa_fwd_deferred(dev["q"], dev["k"], dev["v"], **kw))
+        print(json.dumps({
+            "deferred_pv": True, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+            "kv_range": kv, "single_pass_ms": round(t_one, 4), "deferred_ms": round(t_def, 4),
+            "time_ratio": round(t_def / t_one, 4),
+            "single_pass_tflops": round(w.fwd_flops() / t_one / 1e9, 2),
+            "deferred_tflops": round(w.fwd_flops() / t_def / 1e9, 2)}), flush=True)
 
 
 if __name__ == "__main__":

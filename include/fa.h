@@ -225,6 +225,23 @@ FA_API int fa_bwd_dropout(const void* q, const void* k, const void* v, const flo
                    const int32_t* kv_len, float p, uint64_t seed, uint32_t offset,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Forward pass with the P V product deferred to the end of the key row (an ablation).
+ * "Fewer matrix multiplications, same results, should we consider adopting it?"
+ * (flash-attention issue thread): per query block the numerator blocks of the whole key
+ * row are kept on chip (earlier blocks rescaled when the running maximum rises) and the
+ * output is one product with V at the end, instead of an output update per key block.
+ * The thread's objection is the on-chip room for a query block's whole numerator row:
+ * here it lives in registers, so N <= FA_DEFERRED_MAX_N. The result is the same exact
+ * attention as fa_fwd: same arguments, layouts, outputs and errors, dtype FA_BF16 or
+ * FA_F16 (FA_F32 is FA_EUNSUPPORTED), N > FA_DEFERRED_MAX_N is FA_EINVAL.
+ */
+#define FA_DEFERRED_MAX_N 512
+
+FA_API int fa_fwd_deferred(const void* q, const void* k, const void* v, float* o, float* lse,
+                    int B, int H, int N, int d, float scale, int causal, int dtype,
+                    const int32_t* kv_len, void* stream);
+
 /* Static description of a status code. */
 FA_API const char* fa_status_str(int status);
 

@@ -33,12 +33,13 @@ import torch
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_split_count", "fa_fwd_partial",
            "fa_merge", "fa_fwd_sparse", "fa_bwd_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
-           "FA_SPARSE_BLOCK", "fa_status_str", "fa_last_error", "fa_version", "FaError", "lib_path",
+           "fa_fwd_deferred", "FA_DEFERRED_MAX_N", "FA_SPARSE_BLOCK", "fa_status_str", "fa_last_error", "fa_version", "FaError", "lib_path",
            "load_library",
            "FA_F32", "FA_BF16", "FA_F16"]
 
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_SPARSE_BLOCK = 128
+FA_DEFERRED_MAX_N = 512
 _DTYPE_CODE = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.float16: FA_F16}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -88,6 +89,9 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
                                   i32, i32, vp, vp, vp, sz, vp]
     lib.fa_bwd_sparse.restype = i32
+    lib.fa_fwd_deferred.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, i32, vp,
+                                    vp]
+    lib.fa_fwd_deferred.restype = i32
     u64 = ctypes.c_uint64
     u32 = ctypes.c_uint32
     lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, i32, vp,
@@ -381,3 +385,21 @@ def fa_bwd_dropout(q, k, v, o, dout, lse, *, p, seed, offset=0, causal=False, sc
                                 _stream(q.device, stream))
     _check(st)
     return dq, dk, dv
+
+
+def fa_fwd_deferred(q, k, v, *, causal=False, scale=None, kv_len=None, out=None, lse=None,
+                    stream=None):
+    """Forward pass with the P V product deferred to the end of each query block's key
+    row (N <= FA_DEFERRED_MAX_N): the same (o, lse) as fa_fwd."""
+    B, H, N, d = _shape(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    kv = _kv(kv_len, B, q.device)
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_deferred(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
+                                 scale, int(bool(causal)), _DTYPE_CODE[q.dtype], _ptr(kv),
+                                 _stream(q.device, stream))
+    _check(st)
+    return o, lse_t

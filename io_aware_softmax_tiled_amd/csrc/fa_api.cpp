@@ -117,7 +117,8 @@ int check_dropout(int dtype, float p, Drop* out) {
 
 int fwd_impl(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
              int N, int d, float scale, int causal, int dtype, const int32_t* kv_len,
-             const uint8_t* block_mask, void* stream, const Drop& drop = Drop()) {
+             const uint8_t* block_mask, void* stream, const Drop& drop = Drop(),
+             bool deferred = false) {
   clear_error();
   int st = check_common(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
@@ -147,7 +148,8 @@ int fwd_impl(const void* q, const void* k, const void* v, float* o, float* lse, 
   a.drop_t = drop.t;
   a.seed = drop.seed;
   a.offset = drop.offset;
-  hipError_t e = fa::launch_fwd(a, static_cast<hipStream_t>(stream));
+  hipError_t e = deferred ? fa::launch_fwd_deferred(a, static_cast<hipStream_t>(stream))
+                          : fa::launch_fwd(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_EHIP, "forward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }
@@ -188,6 +190,21 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, float* o, float*
   drop.offset = offset;
   return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, kv_len, nullptr, stream,
                   drop);
+}
+
+int fa_fwd_deferred(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                    int H, int N, int d, float scale, int causal, int dtype,
+                    const int32_t* kv_len, void* stream) {
+  clear_error();
+  int st = check_common(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (dtype == FA_F32)
+    return fail(FA_EUNSUPPORTED, "the deferred-PV forward takes bf16 or f16 inputs, not f32");
+  if (N > FA_DEFERRED_MAX_N)
+    return fail(FA_EINVAL, "N=%d exceeds the deferred-PV limit %d", N, FA_DEFERRED_MAX_N);
+  static_assert(FA_DEFERRED_MAX_N == fa::kDeferredMaxN, "limit mismatch");
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, kv_len, nullptr, stream,
+                  Drop(), true);
 }
 
 int fa_split_count(int N, int split_len) {

@@ -32,7 +32,8 @@ def lib():
 def test_header_declares_the_api():
     assert declared_symbols() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_sparse", "fa_bwd_stage",
                                   "fa_bwd_workspace_size",
-                                  "fa_fwd", "fa_fwd_dropout", "fa_fwd_partial", "fa_fwd_sparse",
+                                  "fa_fwd", "fa_fwd_deferred", "fa_fwd_dropout", "fa_fwd_partial",
+                                  "fa_fwd_sparse",
                                   "fa_last_error", "fa_merge", "fa_split_count",
                                   "fa_status_str", "fa_version"]
 
@@ -293,3 +294,17 @@ def test_dropout_binding_checks_key():
     for seed, offset in ((-1, 0), (1 << 64, 0), (0, 1 << 32), (0, -1)):
         with pytest.raises(ValueError):
             fa.fa_fwd_dropout(q, q, q, p=0.1, seed=seed, offset=offset)
+
+
+# ---- deferred P V --------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,dtype,q,code", [
+    (513, 1, P, FA_EINVAL),
+    (256, 0, P, FA_EUNSUPPORTED),
+    (256, 1, None, FA_EINVAL),
+    (0, 1, P, FA_OK),
+])
+def test_deferred_rejects_before_launch(lib, N, dtype, q, code):
+    st = lib.fa_fwd_deferred(q, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x700000, 1, 1,
+                             N, 64, 0.125, 0, dtype, None, None)
+    assert st == code
