@@ -12,7 +12,7 @@ kernel of the step timed with HIP events on the stream it runs on: fa_bwd is run
 three stages) and the CPU oracle's throughput on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--sweep] [--split-kv] [--sparse]
-                  [--dropout] [--deferred] [--no-cpu-baseline]
+                  [--dropout] [--deferred] [--configs] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -153,6 +153,10 @@ def main():
                     help="also print deferred-PV lines: the forward that keeps a query "
                          "block's whole numerator row on chip and multiplies by V once, "
                          "against the single-pass forward (supplementary)")
+    ap.add_argument("--configs", action="store_true",
+                    help="also print one line per parity workload (1-5): each pass's time, "
+                         "TFLOP/s, % of peak and % of the roofline-attainable rate "
+                         "(supplementary)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy a MIB-MiB buffer once (a plain copy kernel of known size, "
@@ -246,6 +250,8 @@ def main():
         dropout(fa, torch, workloads)
     if args.deferred:
         deferred(fa, torch, workloads)
+    if args.configs:
+        configs(fa, torch, workloads)
 
 
 def sweep(fa, torch, workloads):
@@ -412,6 +418,54 @@ def deferred(fa, torch, workloads):
             "time_ratio": round(t_def / t_one, 4),
             "single_pass_tflops": round(w.fwd_flops() / t_one / 1e9, 2),
             "deferred_tflops": round(w.fwd_flops() / t_def / 1e9, 2)}), flush=True)
+
+
+
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
+
+
+def configs(fa, torch, workloads):
+    """Supplementary lines: every parity workload timed on its own, with the roofline
+    bound of each pass: attainable = min(peak, algorithmic FLOP/byte x 8 TB/s).
+    Algorithmic bytes: forward Q, K, V in, O (fp32) and LSE out; backward Q, K, V, dO,
+    O (fp32), LSE in, D written and read once, dQ, dK, dV (fp32) out."""
+    for wid in sorted(workloads.WORKLOADS):
+        w = workloads.WORKLOADS[wid]
+        inp = workloads.draw(w)
+        dev = {n: (None if inp[n] is None else inp[n].cuda()) for n in ("q", "k", "v", "dout")}
+        kvl = None if inp["kv_len"] is None else inp["kv_len"].cuda()
+        e = 4 if w.dtype == "f32" else 2
+        bhn, bhnd = w.B * w.H * w.N, w.B * w.H * w.N * w.d
+        peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+        kw = dict(causal=w.causal, scale=w.scale, kv_len=kvl)
+        o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+        t_f = _time(torch, lambda: fa.fa_fwd(dev["q"], dev["k"], dev["v"], out=o, lse=lse, **kw))
+        passes = [("fwd", t_f, w.fwd_flops(), 3 * bhnd * e + 4 * bhnd + 4 * bhn)]
+        if w.has_bwd:
+            ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8,
+                             device="cuda")
+            t_b = _time(torch, lambda: fa.fa_bwd(dev["q"], dev["k"], dev["v"], o, dev["dout"], lse,
+                                                 workspace=ws, **kw))
+            passes.append(("bwd", t_b, w.bwd_flops(),
+                           4 * bhnd * e + 4 * bhnd + 4 * bhn + 8 * bhn + 12 * bhnd))
+        eff = None
+        if inp["kv_len"] is not None:   # the work the kernels actually have to do
+            eff = sum(4.0 * w.H * w.N * int(x) * w.d for x in inp["kv_len"].tolist())
+        for name, t, flops, nbytes in passes:
+            tf = flops / t / 1e9
+            attain = min(peak, flops / nbytes * PEAK_HBM_GBS / 1e3)
+            line = {"config": wid, "workload": w.name, "pass": name, "dtype": w.dtype,
+                    "ms": round(t, 4), "tflops": round(tf, 2),
+                    "pct_peak": round(100 * tf / peak, 2),
+                    "bound": "mfma" if attain >= peak else "hbm",
+                    "attainable_tflops": round(attain, 1),
+                    "pct_attainable": round(100 * tf / attain, 2),
+                    "algorithmic_mib": round(nbytes / 2**20, 1)}
+            if eff is not None:
+                mult = 1.0 if name == "fwd" else 2.5
+                line["effective_tflops"] = round(mult * eff / t / 1e9, 2)
+            print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
