@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // dropout: each wave's random bytes of the current tile, [query][its 32 keys]
   __shared__ __attribute__((aligned(16))) uint8_t zbuf[kDropout ? 4 * kBQ * 32 : 16];
 
-  const WgPos pos = wg_position(heads_per_xcd, blockIdx.x);
+  const WgPos pos = wg_position(heads_per_xcd, blockIdx.x, BH);
   const int kblk = pos.blk;  // key block 0 has the most query tiles under a causal mask
   if (pos.bh >= BH || kblk >= n_kblk) return;
   const int bh = pos.bh;
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   __shared__ uint16_t tlist[kSparse ? 2 * kSparseMaxBlocks : 1];  // enabled key tiles
   __shared__ int tlist_len;
 
-  const WgPos pos = wg_position(heads_per_xcd, blockIdx.x);
+  const WgPos pos = wg_position(heads_per_xcd, blockIdx.x, BH);
   if (pos.bh >= BH) return;
   const int mblk = n_mblk - 1 - pos.blk;  // heaviest query block first
   const int bh = pos.bh;
@@ -681,7 +681,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages) {
   const size_t rows = (size_t)BH * a.N;
   const int pre_blocks = (int)((rows * (a.d / 8) + kThreads - 1) / kThreads);
   const float sl2 = a.scale * kLog2e;
-  const int hpx = (BH + 7) / 8;
+  const int hpx = heads_per_xcd(BH);
   const int n_kblk = (a.N + kBK - 1) / kBK;
   const int n_mblk = (a.N + kBM - 1) / kBM;
   const auto* q16 = static_cast<const uint16_t*>(a.q);
@@ -698,13 +698,13 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages) {
       hipLaunchKernelGGL((bwd_pre_kernel<TAG, DIM>), dim3(pre_blocks), dim3(kThreads), 0,    \
                          stream, dO16, a.o, a.delta, rows);                                  \
     if (stages & 2)                                                                          \
-      hipLaunchKernelGGL((bwd_dkdv_kernel<TAG, DIM, SP, DR>), dim3(8 * hpx * n_kblk),        \
+      hipLaunchKernelGGL((bwd_dkdv_kernel<TAG, DIM, SP, DR>), dim3(BH * n_kblk),              \
                          dim3(kThreads), 0, stream, q16, k16, v16, dO16, a.lse, a.delta,     \
                          a.dk, a.dv, BH, a.H, a.N, a.scale, sl2, a.causal, a.kv_len, n_kblk, \
                          hpx, a.block_mask, n_sb, seed_lo, seed_hi, a.offset, a.drop_t,      \
                          keep_scale);                                                        \
     if (stages & 4)                                                                          \
-      hipLaunchKernelGGL((bwd_dq_kernel<TAG, DIM, SP, DR>), dim3(8 * hpx * n_mblk),          \
+      hipLaunchKernelGGL((bwd_dq_kernel<TAG, DIM, SP, DR>), dim3(BH * n_mblk),                \
                          dim3(kThreads), 0, stream, q16, k16, v16, dO16, a.lse, a.delta,     \
                          a.dq, BH, a.H, a.N, a.scale, sl2, a.causal, a.kv_len, n_mblk, hpx,  \
                          a.block_mask, n_sb, seed_lo, seed_hi, a.offset, a.drop_t, keep_scale); \

@@ -86,12 +86,17 @@ template <> __device__ inline u32x4 to_f16x8<BF16>(u32x4 x) {
 // lane's 8 consecutive registers cover 8 consecutive rows
 __device__ inline int kappa(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-// blockIdx.x -> (head, block): XCD-major (blocks of one head on one XCD), block index
-// `slot / heads_per_xcd` from 0
+// blockIdx.x -> (head, block), block index `slot / heads_per_xcd` counted from 0. When
+// B*H is a multiple of 8 (heads_per_xcd = B*H/8) the mapping is XCD-major: consecutive
+// workgroups go to consecutive XCDs, and all blocks of a head land on one XCD so its
+// K/V tiles are shared in that XCD's L2. Otherwise (heads_per_xcd = 0) heads vary
+// fastest, so every XCD still gets an equal share of the work when there are fewer
+// heads than XCDs or they do not divide evenly. Either way the grid is B*H x blocks.
 struct WgPos {
   int bh, blk;
 };
-__device__ inline WgPos wg_position(int heads_per_xcd, int w) {
+__device__ inline WgPos wg_position(int heads_per_xcd, int w, int BH) {
+  if (heads_per_xcd == 0) return {w % BH, w / BH};
   const int xcd = w & 7;
   const int slot = w >> 3;
   return {(slot % heads_per_xcd) * 8 + xcd, slot / heads_per_xcd};

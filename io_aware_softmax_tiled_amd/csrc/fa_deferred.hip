@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kDefThreads, 1) void fwd_deferred_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t Tb0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t Tb1[kTileBytes];
 
-  const WgPos pos = wg_position(heads_per_xcd, blockIdx.x);
+  const WgPos pos = wg_position(heads_per_xcd, blockIdx.x, BH);
   if (pos.bh >= BH) return;
   const int mblk = n_mblk - 1 - pos.blk;  // heaviest query block first
   const int b = pos.bh / H;
@@ -243,8 +243,8 @@ hipError_t launch_fwd_deferred(const FwdArgs& a, hipStream_t stream) {
     return hipErrorInvalidValue;
   const int BH = a.B * a.H;
   const int n_mblk = (a.N + kDefBM - 1) / kDefBM;
-  const int hpx = (BH + 7) / 8;
-  const int blocks = 8 * hpx * n_mblk;
+  const int hpx = heads_per_xcd(BH);
+  const int blocks = BH * n_mblk;
   const float sl2 = a.scale * kLog2e;
   const auto* q16 = static_cast<const uint16_t*>(a.q);
   const auto* k16 = static_cast<const uint16_t*>(a.k);

@@ -37,8 +37,9 @@
 // * Masking touches only the sub-blocks that cross the diagonal, the key-padding bound
 //   or the end of the sequence for a wave; tiles past the workgroup's last visible key
 //   are not visited.
-// * Workgroups are ordered heaviest-first for causal attention, and all query blocks
-//   of a head are placed on one XCD so its K/V tiles are shared in that XCD's L2.
+// * Workgroups are ordered heaviest-first for causal attention; when B*H is a multiple
+//   of 8, all query blocks of a head are placed on one XCD so its K/V tiles are shared
+//   in that XCD's L2 (otherwise heads vary fastest, to keep every XCD busy).
 #include <type_traits>
 
 #include "fa_common.h"
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
     split = blockIdx.x / per_split;
     wid = blockIdx.x - split * per_split;
   }
-  const WgPos pos = wg_position(heads_per_xcd, wid);
+  const WgPos pos = wg_position(heads_per_xcd, wid, BH);
   if (pos.bh >= BH) return;
   const int mblk = n_mblk - 1 - pos.blk;  // heaviest query block first
   const int b = pos.bh / H;
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel_f32(
   __shared__ __attribute__((aligned(16))) float Ks[kBN * kLd];
   __shared__ __attribute__((aligned(16))) float Vs[kBN * kLd];
 
-  const WgPos pos = wg_position(heads_per_xcd, blockIdx.x);
+  const WgPos pos = wg_position(heads_per_xcd, blockIdx.x, BH);
   if (pos.bh >= BH) return;
   const int mblk = n_mblk - 1 - pos.blk;  // heaviest query block first
   const int b = pos.bh / H;
@@ -661,8 +662,8 @@ static int fwd_waves(int B, int H, int N, int d, int dtype) {
 FwdGrid fwd_grid(int B, int H, int N, int waves) {
   FwdGrid g;
   g.n_mblk = (N + 32 * waves - 1) / (32 * waves);
-  g.heads_per_xcd = (B * H + 7) / 8;
-  g.blocks = 8 * g.heads_per_xcd * g.n_mblk;
+  g.heads_per_xcd = heads_per_xcd(B * H);
+  g.blocks = B * H * g.n_mblk;
   return g;
 }
 

@@ -30,6 +30,7 @@ from .attention import (  # noqa: F401
     allowed_mask,
     head_forward,
     head_backward,
+    head_row_block,
     attention_forward,
     attention_backward,
     attention_forward_heads,

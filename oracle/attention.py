@@ -111,6 +111,20 @@ def head_backward(q, k, v, dout, scale, causal=False, kv_len_b=None, check_d=Tru
     return dq, dk, dv
 
 
+def head_row_block(q, k, v, dout, scale, causal, kv_len_b, r0, r1):
+    """The definition restricted to query rows r0 .. r1-1 of one head, for heads too long
+    to take whole: (O, LSE, dQ) of those rows, and their contributions to dK and dV
+    (scale dS^T Q and P^T dO summed over those rows, for every key). It is the body of
+    head_forward / head_backward for one row block; under the causal mask the last row
+    block's contributions are the whole dK and dV of the keys inside it."""
+    q, k, v, dout = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    p, m, l = _probs(q[r0:r1], k, scale, causal, kv_len_b, r0)
+    do = dout[r0:r1]
+    dp = do @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1)[:, None])
+    return (p @ v, m + np.log(l), scale * (ds @ k), scale * (ds.T @ q[r0:r1]), p.T @ do)
+
+
 def _kv(kv_len, b):
     return None if kv_len is None else int(kv_len[b])
 

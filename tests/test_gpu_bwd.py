@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
 from tests import gpu_util as U
 
@@ -122,3 +123,18 @@ def test_bwd_stages_match_fa_bwd():
     torch.cuda.synchronize()
     for a, b in zip(outs2, (dq, dk, dv)):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("B,H", [(1, 1), (1, 3), (3, 5), (2, 6), (1, 9)])
+def test_head_counts_not_multiple_of_8(B, H):
+    """B*H below or off a multiple of 8 (workgroups then spread with heads varying
+    fastest instead of one head per XCD): forward and backward against the oracle."""
+    w, inp = workloads.custom(B, H, 700, 128, "bf16", True, seed=60 + B * H)
+    U.say(f"[bwd] B={B} H={H} N=700 d=128 causal")
+    o, lse, dq, dk, dv = U.gpu_bwd(inp)
+    q, k, v, do = (U.f64(inp, n) for n in ("q", "k", "v", "dout"))
+    ro, rl = oracle.attention_forward(q, k, v, inp["scale"], True)
+    rq, rk, rv = oracle.attention_backward(q, k, v, do, inp["scale"], True)
+    for name, got, ref in (("O", o, ro), ("LSE", lse, rl), ("dQ", dq, rq), ("dK", dk, rk),
+                           ("dV", dv, rv)):
+        U.compare(name, got, ref, "bf16")
