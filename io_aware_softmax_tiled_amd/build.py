@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_merge.hip", "fa_deferred.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_bwd_dkdv.hip", "fa_merge.hip", "fa_deferred.hip",
+           "fa_api.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: never emit packed fp32 VALU (v_pk_{add,mul,fma}_f32).
@@ -25,6 +26,13 @@ HIPCC_FLAGS = [
     "-munsafe-fp-atomics", "-Wall", "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-source additions. The dK/dV kernel (one wave per SIMD, 392 registers) runs about
+# 6% faster with LLVM's iterative ILP scheduler than with the default, measured at
+# B=2 H=16 N=4096 d=128 and B=8 H=16 N=512 d=64; the other kernels are as fast or
+# faster with the default, so the option is confined to that file.
+EXTRA_FLAGS = {
+    "fa_bwd_dkdv.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
 
 
 def hipcc() -> str:
@@ -41,7 +49,8 @@ def build(verbose: bool = False) -> str:
         objs = []
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
-            cmd = [cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+                   "-o", obj]
             if src.endswith(".cpp"):
                 cmd = [cc, "-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
                        "-c", os.path.join(CSRC, src), "-o", obj]

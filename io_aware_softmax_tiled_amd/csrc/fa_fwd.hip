@@ -74,8 +74,6 @@ constexpr int kThreads = 256;
 // byte (i, j) of head bh, with j = 32 g + u, is byte 8 (u / 16) + u % 8 of the
 // Philox4x32-10 block at counter (i, 2 g + (u / 8) % 2, bh, offset) under the key
 // (seed_lo, seed_hi). The statistics (and LSE) are those of the undropped scores.
-constexpr int kSparseBlock = 128;
-constexpr int kSparseMaxBlocks = 2048;  // key blocks per row of the mask (N <= 2^18)
 
 template <typename T, int D, int W, int kMode>
 __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(

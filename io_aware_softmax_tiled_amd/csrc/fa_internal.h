@@ -6,6 +6,11 @@
 
 namespace fa {
 
+// block-sparse mask geometry shared by the kernels: 128 x 128 blocks, at most 2048 per
+// row or column (N <= 2^18; the LDS lists of enabled blocks are sized for it)
+constexpr int kSparseBlock = 128;
+constexpr int kSparseMaxBlocks = 2048;
+
 constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBF16 = 1;
 constexpr int kDtypeF16 = 2;
@@ -84,5 +89,7 @@ struct MergeArgs {
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 // stages: bit 0 = D (bwd_pre), bit 1 = dK/dV, bit 2 = dQ; launched in that order
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages = 7);
+// the dK/dV kernel alone (fa_bwd_dkdv.hip; reads the D that bwd_pre wrote)
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace fa
