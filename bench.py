@@ -9,7 +9,8 @@ that for the backward pass, against the dense bf16 matrix-core peak.
 
 Prints ONE JSON line with the throughput, the roofline of the dominant kernel (each
 kernel of the step timed with HIP events on the stream it runs on: fa_bwd is run as its
-three stages) and the CPU oracle's throughput on a bounded sample of the same workload.
+two stages, dQ with D and then dK/dV) and the CPU oracle's throughput on a bounded
+sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--sweep] [--split-kv] [--sparse]
                   [--dropout] [--deferred] [--configs] [--no-cpu-baseline]
@@ -85,25 +86,29 @@ def cpu_baseline(inp, w, budget_heads=None):
     }
 
 
+# fa_bwd's kernels as fa_bwd_stage calls: stage 3 (dQ, forming and writing D), then
+# stage 1 (dK/dV, reading D)
+BWD_STAGES = (3, 1)
+
+
 def run_step(fa, dev, w, ws, events=None):
-    """fa_fwd, then fa_bwd as its three stages (the same kernels fa_bwd launches, in the
-    same order on the same stream), with events between the kernels when given."""
+    """fa_fwd, then fa_bwd as its stages (the same kernels fa_bwd launches, in the same
+    order on the same stream), with events between the kernels when given."""
     rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
     o, lse = fa.fa_fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale,
                        out=dev["o"], lse=dev["lse"])
     rec(1)
-    for stage in range(3):
+    for i, stage in enumerate(BWD_STAGES):
         fa.fa_bwd_stage(stage, dev["q"], dev["k"], dev["v"], o, dev["dout"], lse, dev["dq"],
                         dev["dk"], dev["dv"], ws, causal=w.causal, scale=w.scale)
-        rec(2 + stage)
+        rec(2 + i)
     return dev["dq"]
 
 
 # kernels of one step, in launch order, and the MFMA FLOPs each performs as a multiple
-# of the nominal forward count (the forward: 2 products; dK/dV: S, dP, dV, dK; dQ: S, dP,
-# dQ; D: none -- it is bound by HBM)
-KERNELS = [("fwd_kernel_16", 1.0), ("bwd_pre_kernel", 0.0), ("bwd_dkdv_kernel", 2.0),
-           ("bwd_dq_kernel", 1.5)]
+# of the nominal forward count (the forward: 2 products; dQ: S, dP, dQ; dK/dV: S, dP,
+# dV, dK)
+KERNELS = [("fwd_kernel_16", 1.0), ("bwd_dq_kernel", 1.5), ("bwd_dkdv_kernel", 2.0)]
 
 
 def bench_workload(fa, torch, w, inp, steps, warmup):
@@ -117,7 +122,8 @@ def bench_workload(fa, torch, w, inp, steps, warmup):
     for _ in range(warmup):
         run_step(fa, dev, w, ws)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)]
+           for _ in range(steps)]
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -126,7 +132,8 @@ def bench_workload(fa, torch, w, inp, steps, warmup):
         run_step(fa, dev, w, ws, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_kernel = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j in range(4)]
+    per_kernel = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
+                  for j in range(len(KERNELS))]
     fwd_ms = per_kernel[0]
     bwd_ms = sum(per_kernel[1:])
     return wall * 1e3 / steps, fwd_ms, bwd_ms, per_kernel
@@ -200,7 +207,7 @@ def main():
             kernels[name]["tflops"] = round(mult * fwd_f / (ms * 1e-3) / 1e12, 2)
     # the dominant kernel of the step: the longest average launch, timed live with HIP
     # events on the stream it runs on; achieved = its own MFMA FLOPs / its time
-    dom = max(range(4), key=lambda j: per_kernel[j])
+    dom = max(range(len(KERNELS)), key=lambda j: per_kernel[j])
     name, mult = KERNELS[dom]
     achieved = mult * fwd_f / (per_kernel[dom] * 1e-3) / 1e12
     roofline = {

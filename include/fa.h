@@ -95,9 +95,10 @@ FA_API size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  * probabilities are recomputed on chip from q, k and lse, tile by tile.
  * workspace: device memory of at least fa_bwd_workspace_size(B,H,N,d) bytes,
  * 256-byte aligned, owned by the caller, contents on entry irrelevant.
- * Three kernels run in order on `stream`: D = rowsum(dout*o) into the workspace,
- * then dk/dv (keys outer), then dq (queries outer); each output is written exactly
- * once, so results are deterministic. dtype must be FA_BF16 or FA_F16 (an FA_F32
+ * Two kernels run in order on `stream`: dq (queries outer), which also forms
+ * D = rowsum(dout*o) for its rows and writes it into the workspace, then dk/dv (keys
+ * outer), which reads D; each output is written exactly once, so results are
+ * deterministic. dtype must be FA_BF16 or FA_F16 (an FA_F32
  * backward is not provided: FA_EUNSUPPORTED).
  */
 FA_API int fa_bwd(const void* q, const void* k, const void* v, const float* o,
@@ -180,12 +181,15 @@ FA_API int fa_bwd_sparse(const void* q, const void* k, const void* v, const floa
                   size_t workspace_bytes, void* stream);
 
 /*
- * One stage of fa_bwd: stage 0 writes D = rowsum(dout * o) into the workspace, stage 1
- * writes dk and dv (reads D), stage 2 writes dq (reads D). fa_bwd is stages 0, 1, 2 in
- * order on one stream; stages 1 and 2 are independent of each other once stage 0 has
- * run, so a caller may also put them on two streams, or time each kernel with events
- * between the calls. Arguments, checks and errors are those of fa_bwd (every pointer is
- * validated even where the stage does not touch it); stage outside 0..2 is FA_EINVAL.
+ * One stage of the backward pass, into caller-allocated outputs: stage 0 writes
+ * D = rowsum(dout * o) into the workspace; stage 1 writes dk and dv (reads D); stage 2
+ * writes dq (it forms D for its own rows from dout and o, and reads nothing from the
+ * workspace); stage 3 is stage 2 that also writes D into the workspace. fa_bwd is
+ * stage 3 then stage 1 on one stream; stages 0, 1, 2 in that order give the same
+ * results bit for bit (both ways of forming D sum in the same order). After stage 0,
+ * stages 1 and 2 are independent and may run on two streams. Arguments, checks and
+ * errors are those of fa_bwd (every pointer is validated even where the stage does not
+ * touch it); stage outside 0..3 is FA_EINVAL.
  */
 FA_API int fa_bwd_stage(int stage, const void* q, const void* k, const void* v,
                  const float* o, const void* dout, const float* lse, float* dq, float* dk,

@@ -213,8 +213,9 @@ def fa_bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, kv_len=None, work
 
 def fa_bwd_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, workspace, *, causal=False,
                  scale=None, kv_len=None, stream=None):
-    """One kernel of fa_bwd into caller-allocated outputs: stage 0 writes D into the
-    workspace, 1 writes dk and dv, 2 writes dq (stages 1 and 2 need stage 0 first)."""
+    """One kernel of the backward pass into caller-allocated outputs: stage 0 writes D
+    into the workspace, 1 writes dk and dv (needs D), 2 writes dq (forms its own D),
+    3 writes dq and D (fa_bwd is stage 3 then stage 1)."""
     B, H, N, d = _shape(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     kv = _kv(kv_len, B, q.device)

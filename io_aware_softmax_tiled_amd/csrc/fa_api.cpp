@@ -300,7 +300,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* o, const 
              const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
              float scale, int causal, int dtype, const int32_t* kv_len,
              const uint8_t* block_mask, void* workspace, size_t workspace_bytes,
-             void* stream, int stages = 7, const Drop& drop = Drop()) {
+             void* stream, int stages = fa::kBwdAll, const Drop& drop = Drop()) {
   clear_error();
   int st = check_common(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
@@ -366,12 +366,14 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const f
                  int H, int N, int d, float scale, int causal, int dtype,
                  const int32_t* kv_len, void* workspace, size_t workspace_bytes,
                  void* stream) {
-  if (stage < 0 || stage > 2) {
+  if (stage < 0 || stage > 3) {
     clear_error();
-    return fail(FA_EINVAL, "stage must be 0 (D), 1 (dK/dV) or 2 (dQ), got %d", stage);
+    return fail(FA_EINVAL, "stage must be 0 (D), 1 (dK/dV), 2 (dQ) or 3 (dQ and D), got %d",
+                stage);
   }
+  static const int kStageBits[4] = {1, 2, 4, 4 | 8};
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, kv_len,
-                  nullptr, workspace, workspace_bytes, stream, 1 << stage);
+                  nullptr, workspace, workspace_bytes, stream, kStageBits[stage]);
 }
 
 int fa_bwd_sparse(const void* q, const void* k, const void* v, const float* o,
@@ -402,7 +404,7 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const float* o,
   drop.seed = seed;
   drop.offset = offset;
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, kv_len,
-                  nullptr, workspace, workspace_bytes, stream, 7, drop);
+                  nullptr, workspace, workspace_bytes, stream, fa::kBwdAll, drop);
 }
 
 }  // extern "C"

@@ -90,9 +90,9 @@ template <typename T, int D, bool kSparse, bool kDropout>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ delta, float* __restrict__ dQ,
-    int BH, int H, int N, float scale, float sl2, int causal,
-    const int* __restrict__ kv_len, int n_mblk, int heads_per_xcd,
+    const float* __restrict__ O, const float* __restrict__ LSE, float* __restrict__ delta,
+    int write_delta, float* __restrict__ dQ, int BH, int H, int N, float scale, float sl2,
+    int causal, const int* __restrict__ kv_len, int n_mblk, int heads_per_xcd,
     const uint8_t* __restrict__ bmask, int n_sb, uint32_t seed_lo, uint32_t seed_hi,
     uint32_t offset, int drop_t, float keep_scale) {
   constexpr int kKC = D / 16;
@@ -181,18 +181,44 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
   if (ntiles > 0) load_tile(0);
 
-  // this lane's query row of Q and dO as B operands (fp16): [query][16c + 8hh + 0..7]
+  // this lane's query row of Q and dO as B operands (fp16): [query][16c + 8hh + 0..7],
+  // and D = rowsum(dO * O) of the row from the same dO and the row of O, summed in the
+  // order of bwd_pre (each 8-element chunk by FMAs in element order, then chunks t and
+  // t ^ off pairwise for off = D/16 .. 1; chunk t = 2c + hh lives in this lane for the
+  // even offsets and in the other half of the wave for off = 1), so the two agree bit
+  // for bit
   u32x4 qf[kKC], of[kKC];
+  float dpart[kKC];
 #pragma unroll
   for (int c = 0; c < kKC; ++c) {
     const size_t off = head + (size_t)qrow_c * D + 16 * c + 8 * hh;
     qf[c] = to_f16x8<T>(*reinterpret_cast<const u32x4*>(Q + off));
-    of[c] = to_f16x8<T>(*reinterpret_cast<const u32x4*>(dO + off));
+    const u32x4 g = *reinterpret_cast<const u32x4*>(dO + off);
+    of[c] = to_f16x8<T>(g);
+    const f32x4 o0 = *reinterpret_cast<const f32x4*>(O + off);
+    const f32x4 o1 = *reinterpret_cast<const f32x4*>(O + off + 4);
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sum = fmaf(to_f32<T>((uint16_t)(g[j] & 0xffff)), j < 2 ? o0[2 * j] : o1[2 * j - 4], sum);
+      sum = fmaf(to_f32<T>((uint16_t)(g[j] >> 16)), j < 2 ? o0[2 * j + 1] : o1[2 * j - 3], sum);
+    }
+    dpart[c] = sum;
   }
+#pragma unroll
+  for (int m = kKC / 2; m > 0; m >>= 1)
+#pragma unroll
+    for (int c = 0; c < kKC; ++c)
+      if (c < (c ^ m)) {
+        const float t2 = dpart[c] + dpart[c ^ m];
+        dpart[c] = t2;
+        dpart[c ^ m] = t2;
+      }
+  const float dlt = sum_halves(dpart[0]);
+  if (write_delta && hh == 0 && qrow < N) delta[(size_t)bh * N + qrow] = dlt;
   // a row that sees no key (LSE = -inf, block-sparse) must give P = 0: +inf here
   const float lse_row = LSE[(size_t)bh * N + qrow_c];
   const float lse2 = lse_row == -INFINITY ? INFINITY : lse_row * kLog2e;
-  const float dlt = delta[(size_t)bh * N + qrow_c];
   f32x16 dqacc[kDB];
 #pragma unroll
   for (int i = 0; i < kDB; ++i)
@@ -333,15 +359,16 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages) {
     if (stages & 1)                                                                          \
       hipLaunchKernelGGL((bwd_pre_kernel<TAG, DIM>), dim3(pre_blocks), dim3(kThreads), 0,    \
                          stream, dO16, a.o, a.delta, rows);                                  \
+    if (stages & 4)                                                                          \
+      hipLaunchKernelGGL((bwd_dq_kernel<TAG, DIM, SP, DR>), dim3(BH * n_mblk),                \
+                         dim3(kThreads), 0, stream, q16, k16, v16, dO16, a.o, a.lse, a.delta, \
+                         (stages & 8) ? 1 : 0, a.dq, BH, a.H, a.N, a.scale, sl2, a.causal,    \
+                         a.kv_len, n_mblk, hpx, a.block_mask, n_sb, seed_lo, seed_hi,         \
+                         a.offset, a.drop_t, keep_scale);                                     \
     if (stages & 2) {                                                                        \
       const hipError_t e = launch_bwd_dkdv(a, stream);                                       \
       if (e != hipSuccess) return e;                                                         \
     }                                                                                        \
-    if (stages & 4)                                                                          \
-      hipLaunchKernelGGL((bwd_dq_kernel<TAG, DIM, SP, DR>), dim3(BH * n_mblk),                \
-                         dim3(kThreads), 0, stream, q16, k16, v16, dO16, a.lse, a.delta,     \
-                         a.dq, BH, a.H, a.N, a.scale, sl2, a.causal, a.kv_len, n_mblk, hpx,  \
-                         a.block_mask, n_sb, seed_lo, seed_hi, a.offset, a.drop_t, keep_scale); \
   } while (0)
 #define FA_BWD_LAUNCH(TAG, DIM)                                          \
   do {                                                                   \

@@ -87,8 +87,11 @@ struct MergeArgs {
   int n_splits, B, H, N, d;
 };
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
-// stages: bit 0 = D (bwd_pre), bit 1 = dK/dV, bit 2 = dQ; launched in that order
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages = 7);
+// stages: bit 0 = D (bwd_pre), bit 2 = dQ (which forms D for its own rows), bit 3 = the
+// dQ kernel also writes D to the workspace, bit 1 = dK/dV (reads D); launched in that
+// order. The whole backward pass is bits 2, 3 and 1: dQ and D in one kernel, then dK/dV.
+constexpr int kBwdAll = 2 | 4 | 8;
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages = kBwdAll);
 // the dK/dV kernel alone (fa_bwd_dkdv.hip; reads the D that bwd_pre wrote)
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 

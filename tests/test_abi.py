@@ -245,7 +245,7 @@ def test_bwd_stage_rejects_before_launch(lib):
     args = [P, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x400000, P + 0x500000,
             P + 0x600000, P + 0x700000, P + 0x800000, 1, 1, 64, 64, 0.125, 0, 1, None]
     ws = lib.fa_bwd_workspace_size(1, 1, 64, 64)
-    for bad in (-1, 3, 7):
+    for bad in (-1, 4, 7):
         assert lib.fa_bwd_stage(bad, *args, P + 0x900000, ws, None) == FA_EINVAL
     assert lib.fa_bwd_stage(1, *args, None, 0, None) == FA_EWORKSPACE
     args[15] = 0  # f32

@@ -99,7 +99,7 @@ def test_bwd_deterministic():
 
 def test_bwd_stages_match_fa_bwd():
     """fa_bwd_stage 0, 1, 2 give fa_bwd's results bit for bit, also with stages 1 and 2
-    on two streams."""
+    on two streams, and so do stages 3, 1 (dQ forming and writing D, then dK/dV)."""
     import io_aware_softmax_tiled_amd as fa
     w, inp = workloads.custom(2, 3, 700, 128, "bf16", True, kv_range=(350, 700), seed=25)
     dev = U.to_dev(inp)
@@ -122,6 +122,15 @@ def test_bwd_stages_match_fa_bwd():
                     stream=side, **kw)
     torch.cuda.synchronize()
     for a, b in zip(outs2, (dq, dk, dv)):
+        assert torch.equal(a, b)
+    # stage 3 (dQ writing D) then stage 1 is what fa_bwd runs; D from either stage is the
+    # same bits
+    outs3 = [torch.full_like(dq, float("nan")) for _ in range(3)]
+    ws.fill_(255)
+    for st in (3, 1):
+        fa.fa_bwd_stage(st, dev["q"], dev["k"], dev["v"], o, dev["dout"], lse, *outs3, ws, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(outs3, (dq, dk, dv)):
         assert torch.equal(a, b)
 
 
