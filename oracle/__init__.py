@@ -50,6 +50,7 @@ from .sparse import (  # noqa: F401
     block_allowed,
     head_forward_sparse,
     head_backward_sparse,
+    head_row_block_sparse,
     attention_forward_sparse,
     attention_backward_sparse,
 )

@@ -92,3 +92,24 @@ def attention_backward_sparse(q, k, v, dout, scale, causal=False, kv_len=None,
             dq[b, h], dk[b, h], dv[b, h] = head_backward_sparse(
                 q[b, h], k[b, h], v[b, h], dout[b, h], scale, causal, kvb, block_mask, block)
     return dq, dk, dv
+
+
+def head_row_block_sparse(q, k, v, dout, scale, causal, kv_len_b, block_mask, r0, r1,
+                          block=128):
+    """Block-sparse attention restricted to query rows r0 .. r1-1 of one head, for heads
+    too long to take whole: (O, LSE, dQ) of those rows and their contributions to dK and
+    dV, under the same conventions as head_forward_sparse / head_backward_sparse (a row
+    that sees no key: O = 0, LSE = -inf, P = 0)."""
+    q, k, v, dout = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    bm = np.asarray(block_mask) != 0
+    n = k.shape[0]
+    rows = np.arange(r0, r1)
+    cols = np.arange(n)
+    a = allowed_mask(r1 - r0, n, causal, kv_len_b, r0) & bm[(rows // block)[:, None],
+                                                           (cols // block)[None, :]]
+    p, m, l, seen = _probs(q[r0:r1], k, scale, a)
+    lse = np.where(seen, m + np.log(np.where(seen, l, 1.0)), -np.inf)
+    do = dout[r0:r1]
+    dp = do @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1)[:, None])
+    return p @ v, lse, scale * (ds @ k), scale * (ds.T @ q[r0:r1]), p.T @ do

@@ -169,3 +169,30 @@ def test_mask_mutants_are_caught(monkeypatch, mutant):
     except AssertionError:
         caught = True
     assert caught, f"{mutant.__name__} was not caught"
+
+
+@pytest.mark.parametrize("causal,kvb", [(False, None), (True, None), (False, 23), (True, 30)])
+def test_row_block_sparse_stitches_to_the_head_functions(causal, kvb):
+    """head_row_block_sparse over row blocks (ragged, some rows with no visible key)
+    reproduces head_forward_sparse and head_backward_sparse, which the tests above pin."""
+    rng = np.random.default_rng(40)
+    N, d, blk = 37, 5, 8
+    q, k, v, do = (rng.standard_normal((N, d)) for _ in range(4))
+    nb = -(-N // blk)
+    m = (rng.random((nb, nb)) < 0.6).astype(np.uint8)
+    m[1] = 0                                         # a block row with no visible key
+    ro, rl = oracle.head_forward_sparse(q, k, v, 0.7, causal, kvb, m, blk)
+    rq, rk, rv = oracle.head_backward_sparse(q, k, v, do, 0.7, causal, kvb, m, blk)
+    o, lse, dq = np.empty_like(ro), np.empty_like(rl), np.empty_like(rq)
+    dk, dv = np.zeros_like(rk), np.zeros_like(rv)
+    for r0 in range(0, N, 6):
+        r1 = min(N, r0 + 6)
+        o[r0:r1], lse[r0:r1], dq[r0:r1], dkp, dvp = oracle.head_row_block_sparse(
+            q, k, v, do, 0.7, causal, kvb, m, r0, r1, blk)
+        dk += dkp
+        dv += dvp
+    assert np.array_equal(np.isneginf(lse), np.isneginf(rl))
+    fin = ~np.isneginf(rl)
+    assert np.abs(lse[fin] - rl[fin]).max() < 1e-12
+    for a, b in ((o, ro), (dq, rq), (dk, rk), (dv, rv)):
+        assert np.abs(a - b).max() < 1e-12
