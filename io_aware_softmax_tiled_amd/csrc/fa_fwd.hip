@@ -36,7 +36,9 @@
 //   rare; the final division uses the same reference, so the result is unchanged.
 // * Masking touches only the sub-blocks that cross the diagonal, the key-padding bound
 //   or the end of the sequence for a wave; tiles past the workgroup's last visible key
-//   are not visited.
+//   are not visited, and a wave skips the products of sub-blocks past its own last
+//   visible key. Under the causal mask the two waves of each SIMD take a short and a
+//   long row group, so the SIMDs share the diagonal tiles' work evenly.
 // * Workgroups are ordered heaviest-first for causal attention; when B*H is a multiple
 //   of 8, all query blocks of a head are placed on one XCD so its K/V tiles are shared
 //   in that XCD's L2 (otherwise heads vary fastest, to keep every XCD busy).
@@ -142,7 +144,11 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int qi = lane & 31;
   const int hh = lane >> 5;
-  const int wq0 = m0 + wave * 32;              // first query row of this wave
+  // Waves w and w + 4 share a SIMD. With 8 waves the second four take the row groups in
+  // reverse order (4 -> 7, ..., 7 -> 4), so under the causal mask each SIMD holds one
+  // short and one long row group and the SIMDs finish the diagonal tiles together.
+  const int wrow = (W == 8 && wave >= 4) ? 11 - wave : wave;
+  const int wq0 = m0 + wrow * 32;              // first query row of this wave
   const int qrow = wq0 + qi;
   const int qrow_c = min(qrow, N - 1);
 
@@ -176,6 +182,16 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
     }
     __syncthreads();
     ntiles = 2 * blist_len;
+  }
+
+  // 32-key sub-blocks (from kbeg) holding a key that some row of this wave can see:
+  // under the causal mask or a key bound the trailing sub-blocks of the workgroup's
+  // range may hold none, and the wave then skips their products and exponentials
+  // (it still takes part in the tile staging and the barriers)
+  int ns_live = 2 * ntiles;
+  if constexpr (!kSparse) {
+    const int wave_kend = causal ? min(kv_hi, wq0 + 32) : kv_hi;
+    ns_live = __builtin_amdgcn_readfirstlane(min(ns_live, max(0, (wave_kend - kbeg + 31) / 32)));
   }
 
   if constexpr (kGuard) {
@@ -425,16 +441,19 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
 
   barrier_lds();  // tiles 0 and 1 visible
   read_k((const FA_LDS uint8_t*)Kb0, 0);
-  f32x16 S = scores();
-  mask(S, 0);
-  rescale(rowmax(S));
+  f32x16 S;
+  if (ns_live > 0) {
+    S = scores();
+    mask(S, 0);
+    rescale(rowmax(S));
+  }
   read_k((const FA_LDS uint8_t*)Kb0, 1);
 
   // One key tile = two sub-blocks; tile t lives in buffers t%3. After the barrier that
   // opens step t every wave is done with tile t-1, so tile t+2 (held in registers) is
-  // written into its buffers and tile t+3 is fetched. Every wave walks the whole tile
-  // range of the workgroup; sub-blocks past its own diagonal are masked (the one after
-  // the last tile is masked entirely).
+  // written into its buffers and tile t+3 is fetched. Every wave stages every tile of
+  // the workgroup's range; inside its last tiles (step_tail below) it skips the
+  // sub-blocks that hold no key visible to it and masks the rest.
   auto step = [&](int t, const FA_LDS uint8_t* Ka, const FA_LDS uint8_t* Va,
                   const FA_LDS uint8_t* Kn, FA_LDS uint8_t* Kw, FA_LDS uint8_t* Vw) {
     barrier_lds();
@@ -471,16 +490,55 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
     rescale(mx);
   };
 
-  for (int t = 0; t < ntiles; t += 3) {
+  // The same step for the wave's last tiles, where a sub-block may hold no key visible
+  // to the wave: each product and its vector work runs only for live sub-blocks, and
+  // the buffers are chosen at run time (these steps are few, so they are not unrolled).
+  auto step_tail = [&](int t) {
+    const int r = t % 3;
+    const FA_LDS uint8_t* Va = r == 0 ? (const FA_LDS uint8_t*)Vb0
+                             : r == 1 ? (const FA_LDS uint8_t*)Vb1 : (const FA_LDS uint8_t*)Vb2;
+    const FA_LDS uint8_t* Kn = r == 0 ? (const FA_LDS uint8_t*)Kb1
+                             : r == 1 ? (const FA_LDS uint8_t*)Kb2 : (const FA_LDS uint8_t*)Kb0;
+    FA_LDS uint8_t* Kw = r == 0 ? (FA_LDS uint8_t*)Kb2 : r == 1 ? (FA_LDS uint8_t*)Kb0 : (FA_LDS uint8_t*)Kb1;
+    FA_LDS uint8_t* Vw = r == 0 ? (FA_LDS uint8_t*)Vb2 : r == 1 ? (FA_LDS uint8_t*)Vb0 : (FA_LDS uint8_t*)Vb1;
+    const bool l0 = 2 * t < ns_live, l1 = 2 * t + 1 < ns_live, l2 = 2 * t + 2 < ns_live;
+    barrier_lds();
+    store_kv(Kw, Vw);
+    load_kv(min(t + 3, tlast));
+
+    uint32_t pk[8];
+    f32x16 Sn = S;
+    if (l1) Sn = scores();
+    if (l0) expo(S, pk, 2 * t);
+    read_v(Va, 0);
+    if (l1) mask(Sn, 2 * t + 1);
+    if (l0) pv(pk);
+    read_k(Kn, 0);
+    if (l1) rescale(rowmax(Sn));
+
+    if (l2) S = scores();
+    if (l1) expo(Sn, pk, 2 * t + 1);
+    read_v(Va, 1);
+    if (l2) mask(S, 2 * t + 2);
+    if (l1) pv(pk);
+    read_k(Kn, 1);
+    if (l2) rescale(rowmax(S));
+  };
+
+  // tiles t < t_hot have all three sub-blocks 2t, 2t+1, 2t+2 live for this wave
+  const int t_hot = ns_live > 0 ? (ns_live - 1) / 2 : 0;
+  int t = 0;
+  for (; t < t_hot; t += 3) {
     step(t, (const FA_LDS uint8_t*)Kb0, (const FA_LDS uint8_t*)Vb0,
          (const FA_LDS uint8_t*)Kb1, (FA_LDS uint8_t*)Kb2, (FA_LDS uint8_t*)Vb2);
-    if (t + 1 < ntiles)
-      step(t + 1, (const FA_LDS uint8_t*)Kb1, (const FA_LDS uint8_t*)Vb1,
-           (const FA_LDS uint8_t*)Kb2, (FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Vb0);
-    if (t + 2 < ntiles)
-      step(t + 2, (const FA_LDS uint8_t*)Kb2, (const FA_LDS uint8_t*)Vb2,
-           (const FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Kb1, (FA_LDS uint8_t*)Vb1);
+    if (t + 1 >= t_hot) { t += 1; break; }
+    step(t + 1, (const FA_LDS uint8_t*)Kb1, (const FA_LDS uint8_t*)Vb1,
+         (const FA_LDS uint8_t*)Kb2, (FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Vb0);
+    if (t + 2 >= t_hot) { t += 2; break; }
+    step(t + 2, (const FA_LDS uint8_t*)Kb2, (const FA_LDS uint8_t*)Vb2,
+         (const FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Kb1, (FA_LDS uint8_t*)Vb1);
   }
+  for (; t < ntiles; ++t) step_tail(t);
 
   // epilogue: O = O_acc / l, LSE = scale*m_ref + ln(l)
   const float ltot = sum_halves(lsum);
