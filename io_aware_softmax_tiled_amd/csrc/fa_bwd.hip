@@ -152,7 +152,10 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(
   };
   const int qi = lane & 31, hh = lane >> 5;
   const int g = lane >> 4, gi = lane & 15;
-  const int wq0 = m0 + wave * 32;
+  // waves w and w + 4 share a SIMD: with 8 waves the second four take the row groups
+  // in reverse order, so under the causal mask each SIMD holds a short and a long one
+  const int wrow = (W == 8 && wave >= 4) ? 11 - wave : wave;
+  const int wq0 = m0 + wrow * 32;
   const int qrow = wq0 + qi;
   const int qrow_c = min(qrow, N - 1);
 
