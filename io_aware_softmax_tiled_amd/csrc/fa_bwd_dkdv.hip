@@ -216,13 +216,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       dp = Mfma<F16>::run(lds_read16(Oc + off), vf[c], dp);
     }
   };
-  // -inf where the query does not see this lane's key (diagonal, padding, sequence end)
+  // -inf where the query does not see this lane's key (diagonal, padding, sequence end).
+  // Register r of half hf holds query base + 16*(r/8) + r%8 with base = q0 + 32*hf +
+  // 8*hh; the queries that see the lane's key are one window [lo, hi) of those offsets
+  // (empty for a padded key), so each entry costs one unsigned compare against it.
   auto mask = [&](f32x16& s, int q0, int hf) {
+    const int base = q0 + 32 * hf + 8 * hh;
+    const int lo = (causal ? key : 0) - base;
+    const int hi = key < kv_lim ? N - base : lo;
+    const uint32_t span = (uint32_t)max(hi - lo, 0);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int qq = q0 + 32 * hf + 16 * (r >> 3) + 8 * hh + (r & 7);
-      const bool hide = qq >= N || key >= kv_lim || (causal && key > qq);
-      s[r] = hide ? -INFINITY : s[r];
+      const int rel = 16 * (r >> 3) + (r & 7);
+      s[r] = (uint32_t)(rel - lo) < span ? s[r] : -INFINITY;
     }
   };
   FA_LDS uint8_t* zw = (FA_LDS uint8_t*)zbuf + (kDropout ? wave * kBQ * 32 : 0);  // wave bytes
