@@ -224,7 +224,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
     else
       return kbeg + t * kBN;
   };
-  auto load_kv = [&](int t) {
+  auto load_kv_to = [&](int t, u32x4 (&kd)[kVChunks], u32x4 (&vd)[kVChunks]) {
     const int n0 = tile_key(t);
     // (a sparse list may name a tile past the end of the sequence: zero bytes)
     const uint32_t bytes = (uint32_t)max(N - n0, 0) * D * 2;
@@ -232,21 +232,28 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
     const auto rv = buffer_rsrc(v + (size_t)n0 * D, bytes);
 #pragma unroll
     for (int j = 0; j < kVChunks; ++j) {
-      ks[j] = buffer_load16(rk, ld_off[j]);
-      vs[j] = buffer_load16(rv, ld_off[j]);
+      kd[j] = buffer_load16(rk, ld_off[j]);
+      vd[j] = buffer_load16(rv, ld_off[j]);
     }
   };
-  auto store_kv = [&](FA_LDS uint8_t* kb, FA_LDS uint8_t* vb) {
+  auto load_kv = [&](int t) { load_kv_to(t, ks, vs); };
+  auto store_kv_from = [&](FA_LDS uint8_t* kb, FA_LDS uint8_t* vb, const u32x4 (&kd)[kVChunks],
+                           const u32x4 (&vd)[kVChunks]) {
 #pragma unroll
     for (int j = 0; j < kVChunks; ++j) {
       const int ci = tid + kThr * j;
       const int row = ci / kCPR, ch = ci % kCPR;
-      lds_write16(kb + tile_off<D>(row, ch), ks[j]);
-      lds_write16(vb + tile_off<D>(row, ch), to_f16x8<T>(vs[j]));
+      lds_write16(kb + tile_off<D>(row, ch), kd[j]);
+      lds_write16(vb + tile_off<D>(row, ch), to_f16x8<T>(vd[j]));
     }
   };
+  auto store_kv = [&](FA_LDS uint8_t* kb, FA_LDS uint8_t* vb) { store_kv_from(kb, vb, ks, vs); };
   const int tlast = ntiles - 1;
+  // tiles 0 and 1 are fetched together (tile 1 into registers used only here), so the
+  // workgroup waits for one global-memory latency before its first product, not two
+  u32x4 ks1[kVChunks], vs1[kVChunks];
   load_kv(0);
+  load_kv_to(min(1, tlast), ks1, vs1);
 
   // Q fragment: B operand of S^T = K Q^T, lane (qi, hh) holds Q[qrow][16c + 8hh + 0..7]
   u32x4 qf[kKC];
@@ -280,9 +287,8 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
                     8 * (gi & 1);
 
   store_kv((FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Vb0);  // tile 0
-  load_kv(min(1, tlast));
-  store_kv((FA_LDS uint8_t*)Kb1, (FA_LDS uint8_t*)Vb1);  // tile 1 (clamped)
   load_kv(min(2, tlast));
+  store_kv_from((FA_LDS uint8_t*)Kb1, (FA_LDS uint8_t*)Vb1, ks1, vs1);  // tile 1 (clamped)
 
   // The key axis is walked in 32-key sub-blocks (the tiled recurrence with tile width
   // 32), software-pipelined so each region pairs matrix-core work with vector work of
