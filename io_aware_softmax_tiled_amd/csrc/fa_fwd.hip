@@ -448,7 +448,9 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
   barrier_lds();  // tiles 0 and 1 visible
   read_k((const FA_LDS uint8_t*)Kb0, 0);
   f32x16 S;
-  if (ns_live > 0) {
+  // (head_dim 64 runs every sub-block through the full step, so its first scores are
+  // always formed; a sub-block nobody in the wave sees is masked to -inf there)
+  if (D == 64 || ns_live > 0) {
     S = scores();
     mask(S, 0);
     rescale(rowmax(S));
@@ -531,6 +533,21 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
     if (l2) rescale(rowmax(S));
   };
 
+  if constexpr (D == 64) {
+    // head_dim 64 keeps every tile on the full step: the tail steps' extra registers
+    // would push it past 128 VGPRs and halve its occupancy (two 8-wave workgroups per
+    // CU); sub-blocks past a wave's diagonal are masked instead of skipped
+    for (int t = 0; t < ntiles; t += 3) {
+      step(t, (const FA_LDS uint8_t*)Kb0, (const FA_LDS uint8_t*)Vb0,
+           (const FA_LDS uint8_t*)Kb1, (FA_LDS uint8_t*)Kb2, (FA_LDS uint8_t*)Vb2);
+      if (t + 1 < ntiles)
+        step(t + 1, (const FA_LDS uint8_t*)Kb1, (const FA_LDS uint8_t*)Vb1,
+             (const FA_LDS uint8_t*)Kb2, (FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Vb0);
+      if (t + 2 < ntiles)
+        step(t + 2, (const FA_LDS uint8_t*)Kb2, (const FA_LDS uint8_t*)Vb2,
+             (const FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Kb1, (FA_LDS uint8_t*)Vb1);
+    }
+  } else {
   // tiles t < t_hot have all three sub-blocks 2t, 2t+1, 2t+2 live for this wave
   const int t_hot = ns_live > 0 ? (ns_live - 1) / 2 : 0;
   int t = 0;
@@ -545,6 +562,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
          (const FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Kb1, (FA_LDS uint8_t*)Vb1);
   }
   for (; t < ntiles; ++t) step_tail(t);
+  }
 
   // epilogue: O = O_acc / l, LSE = scale*m_ref + ln(l)
   const float ltot = sum_halves(lsum);
