@@ -548,20 +548,20 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
              (const FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Kb1, (FA_LDS uint8_t*)Vb1);
     }
   } else {
-  // tiles t < t_hot have all three sub-blocks 2t, 2t+1, 2t+2 live for this wave
-  const int t_hot = ns_live > 0 ? (ns_live - 1) / 2 : 0;
-  int t = 0;
-  for (; t < t_hot; t += 3) {
-    step(t, (const FA_LDS uint8_t*)Kb0, (const FA_LDS uint8_t*)Vb0,
-         (const FA_LDS uint8_t*)Kb1, (FA_LDS uint8_t*)Kb2, (FA_LDS uint8_t*)Vb2);
-    if (t + 1 >= t_hot) { t += 1; break; }
-    step(t + 1, (const FA_LDS uint8_t*)Kb1, (const FA_LDS uint8_t*)Vb1,
-         (const FA_LDS uint8_t*)Kb2, (FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Vb0);
-    if (t + 2 >= t_hot) { t += 2; break; }
-    step(t + 2, (const FA_LDS uint8_t*)Kb2, (const FA_LDS uint8_t*)Vb2,
-         (const FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Kb1, (FA_LDS uint8_t*)Vb1);
-  }
-  for (; t < ntiles; ++t) step_tail(t);
+    // tiles t < t_hot have all three sub-blocks 2t, 2t+1, 2t+2 live for this wave
+    const int t_hot = ns_live > 0 ? (ns_live - 1) / 2 : 0;
+    int t = 0;
+    for (; t < t_hot; t += 3) {
+      step(t, (const FA_LDS uint8_t*)Kb0, (const FA_LDS uint8_t*)Vb0,
+           (const FA_LDS uint8_t*)Kb1, (FA_LDS uint8_t*)Kb2, (FA_LDS uint8_t*)Vb2);
+      if (t + 1 >= t_hot) { t += 1; break; }
+      step(t + 1, (const FA_LDS uint8_t*)Kb1, (const FA_LDS uint8_t*)Vb1,
+           (const FA_LDS uint8_t*)Kb2, (FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Vb0);
+      if (t + 2 >= t_hot) { t += 2; break; }
+      step(t + 2, (const FA_LDS uint8_t*)Kb2, (const FA_LDS uint8_t*)Vb2,
+           (const FA_LDS uint8_t*)Kb0, (FA_LDS uint8_t*)Kb1, (FA_LDS uint8_t*)Vb1);
+    }
+    for (; t < ntiles; ++t) step_tail(t);
   }
 
   // epilogue: O = O_acc / l, LSE = scale*m_ref + ln(l)
