@@ -183,8 +183,8 @@ def main():
                          "to calibrate HBM byte counters in a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(heads shard across GPUs with no exchange; see DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path (attention heads "
+              "would shard across GPUs with no exchange between them).", file=sys.stderr)
         sys.exit(2)
 
     import torch
