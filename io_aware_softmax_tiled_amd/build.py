@@ -49,8 +49,12 @@ def build(verbose: bool = False) -> str:
         objs = []
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
-            cmd = [cc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
-                   "-o", obj]
+            # a fixed compilation-unit id (clang derives one from the paths otherwise, and
+            # the build directory is a fresh temporary one), so rebuilding the same sources
+            # gives the same library bytes
+            cuid = "fa_" + src.replace(".", "_")
+            cmd = [cc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), f"-cuid={cuid}", "-c",
+                   os.path.join(CSRC, src), "-o", obj]
             if src.endswith(".cpp"):
                 cmd = [cc, "-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
                        "-c", os.path.join(CSRC, src), "-o", obj]
