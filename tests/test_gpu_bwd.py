@@ -59,6 +59,24 @@ def test_bwd_small(dtype, d, N, causal, pad):
         U.compare(name, _sel(t, heads), _stack(ref, heads, i), dtype)
 
 
+@pytest.mark.parametrize("N", [447, 511, 575, 703])
+def test_causal_padded_mid_sizes(N):
+    """Causal with key padding at head_dim 128 over two or three 256-row query blocks: the
+    forward's per-wave tail steps begin at every tile offset modulo the three LDS buffers,
+    some waves' rows run past N, and the 8-wave row groups are paired per SIMD in the
+    forward and dQ kernels. O, LSE and all three gradients against the oracle."""
+    w, inp = workloads.custom(2, 2, N, 128, "bf16", True, kv_range=(N // 3, N), seed=300 + N)
+    U.say(f"[bwd] causal padded mid-size N={N} kv_len={inp['kv_len'].tolist()}")
+    o, lse, dq, dk, dv = U.gpu_bwd(inp)
+    heads = [(b, h) for b in range(2) for h in range(2)]
+    ref_f = U.oracle_fwd(inp, workers=1)
+    U.compare("O", _sel(o, heads), _stack(ref_f, heads, 0), "bf16")
+    U.compare("LSE", _sel(lse, heads), _stack(ref_f, heads, 1), "bf16")
+    ref = U.oracle_bwd(inp, workers=1)
+    for name, t, i in (("dQ", dq, 0), ("dK", dk, 1), ("dV", dv, 2)):
+        U.compare(name, _sel(t, heads), _stack(ref, heads, i), "bf16")
+
+
 def test_bwd_peaky_long():
     """Q x4 (peaky softmax) over 1100 keys, causal, d=128: the config-4 regime at a size
     the oracle checks in full."""
