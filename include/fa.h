@@ -208,7 +208,7 @@ FA_API int fa_bwd_stage(int stage, const void* q, const void* k, const void* v,
  * (seed mod 2^32, seed >> 32). Keys fall in groups of 32: for element (batch b, head h,
  * query i, key j = 32 g + u) the random byte is byte 8*(u/16) + u%8 (little-endian over
  * the four 32-bit output words) of the block at counter (i, 2g + (u/8)%2, b*H + h,
- * offset). With t = round(256 p) (at most 255) an element is kept iff its byte >= t, and
+ * offset). With t = fa_dropout_threshold(p) an element is kept iff its byte >= t, and
  * kept probabilities are scaled by 256 / (256 - t):
  *   o = (P * Z * 256/(256 - t)) v, lse = log-sum-exp of the undropped scaled scores.
  * fa_bwd_dropout computes the gradients of that o with the same mask (same p, seed and
@@ -218,6 +218,14 @@ FA_API int fa_bwd_stage(int stage, const void* q, const void* k, const void* v,
  * a pure function of (seed, offset, b*H + h, i, j): calls with the same key reproduce it,
  * whatever the launch order.
  */
+/*
+ * The byte threshold t of dropout probability p: the t in [0, 255] whose keep probability
+ * (256 - t)/256 lies nearest to 1 - p on the 1/256 grid (t = floor(256 p + 1/2) evaluated
+ * in double precision from the float p, capped at 255), or -1 when p is not in [0, 1).
+ * Host-only and pure; the dropout entry points derive their mask threshold with it.
+ */
+FA_API int fa_dropout_threshold(float p);
+
 FA_API int fa_fwd_dropout(const void* q, const void* k, const void* v, float* o, float* lse,
                    int B, int H, int N, int d, float scale, int causal, int dtype,
                    const int32_t* kv_len, float p, uint64_t seed, uint32_t offset,

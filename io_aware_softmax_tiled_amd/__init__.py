@@ -33,7 +33,7 @@ import torch
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_split_count", "fa_fwd_partial",
            "fa_merge", "fa_fwd_sparse", "fa_bwd_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
-           "fa_fwd_deferred", "FA_DEFERRED_MAX_N", "FA_SPARSE_BLOCK", "fa_status_str", "fa_last_error", "fa_version", "FaError", "lib_path",
+           "fa_fwd_deferred", "fa_dropout_threshold", "FA_DEFERRED_MAX_N", "FA_SPARSE_BLOCK", "fa_status_str", "fa_last_error", "fa_version", "FaError", "lib_path",
            "load_library",
            "FA_F32", "FA_BF16", "FA_F16"]
 
@@ -100,6 +100,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
                                    i32, i32, vp, f32, u64, u32, vp, sz, vp]
     lib.fa_bwd_dropout.restype = i32
+    lib.fa_dropout_threshold.argtypes = [f32]
+    lib.fa_dropout_threshold.restype = i32
     lib.fa_status_str.argtypes = [i32]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -124,6 +126,12 @@ def fa_version() -> int:
 
 def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
     return int(load_library().fa_bwd_workspace_size(B, H, N, d))
+
+
+def fa_dropout_threshold(p: float) -> int:
+    """Byte threshold t of dropout probability p (keep iff byte >= t), -1 if p is not in
+    [0, 1)."""
+    return int(load_library().fa_dropout_threshold(float(p)))
 
 
 def fa_split_count(N: int, split_len: int) -> int:

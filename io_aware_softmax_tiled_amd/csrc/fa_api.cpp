@@ -82,6 +82,12 @@ int fa_version(void) { return 100; /* 0.1.0 */ }
 
 }  // extern "C"
 
+extern "C" int fa_dropout_threshold(float p) {
+  if (!(p >= 0.0f && p < 1.0f)) return -1;
+  const int t = (int)std::floor(256.0 * (double)p + 0.5);
+  return t < 255 ? t : 255;
+}
+
 namespace {
 
 size_t sparse_mask_bytes(int N) {
@@ -105,13 +111,13 @@ struct Drop {
   uint32_t offset = 0;
 };
 
-// t = round(256 p), keep iff the element's random byte >= t.
+// keep iff the element's random byte >= t = fa_dropout_threshold(p)
 int check_dropout(int dtype, float p, Drop* out) {
   if (dtype == FA_F32)
     return fail(FA_EUNSUPPORTED, "attention with dropout takes bf16 or f16 inputs, not f32");
-  if (!(p >= 0.0f && p < 1.0f)) return fail(FA_EINVAL, "dropout p=%g is not in [0, 1)", p);
-  const int t = (int)std::floor(256.0 * (double)p + 0.5);
-  out->t = t < 255 ? t : 255;
+  const int t = fa_dropout_threshold(p);
+  if (t < 0) return fail(FA_EINVAL, "dropout p=%g is not in [0, 1)", p);
+  out->t = t;
   return FA_OK;
 }
 

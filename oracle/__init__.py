@@ -39,6 +39,7 @@ from .attention import (  # noqa: F401
 from .dropout import (  # noqa: F401
     philox4x32,
     dropout_threshold,
+    keep_scale,
     random_bytes,
     keep_mask,
     head_forward_dropout,

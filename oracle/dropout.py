@@ -25,9 +25,12 @@ Readings (where the pages are silent):
   block gives 16 bytes (its four words, little-endian). Key u takes block 2g + ((u >> 3)
   & 1), byte 8*(u >> 4) + (u & 7): keys 0-7 and 16-23 of the group read bytes 0-7 and
   8-15 of the first block, keys 8-15 and 24-31 those of the second.
-- p is quantised to t = round(256 p) (0 <= t <= 255); Z_ij = 1 iff the byte >= t; the
-  keep probability is (256 - t)/256 and the kept probabilities are scaled by its inverse
-  256/(256 - t), so E[Z / keep] = 1 exactly.
+- p is quantised to the byte threshold t whose keep probability (256 - t)/256 lies
+  nearest to 1 - p on the 1/256 grid, i.e. t = round(256 p) with halves rounded up,
+  capped at 255; Z_ij = 1 iff the byte >= t; the kept probabilities are scaled by the
+  inverse of the keep probability, 256/(256 - t), so E[Z / keep] = 1 exactly. p is a
+  32-bit float parameter of the library's entry points, so t is derived from p rounded
+  to float32 (then 256 p + 1/2 in float64, floored), the same arithmetic on both sides.
 - Backward: the chain rule of L = sum(dO * O) through O = (P * Z / keep) V:
   dV = (P * Z / keep)^T dO, dP = (Z / keep) * (dO V^T), D_i = sum_j P_ij dP_ij
   (= sum_k dO_ik O_ik), dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
@@ -59,10 +62,17 @@ def philox4x32(c0, c1, c2, c3, k0, k1, rounds=10):
 
 
 def dropout_threshold(p: float) -> int:
-    """t = round(256 p), the byte threshold (keep iff byte >= t)."""
-    if not 0.0 <= p < 1.0:
+    """The byte threshold t (keep iff byte >= t): round(256 p), halves up, at most 255,
+    with p taken as the float32 the entry points receive."""
+    p32 = float(np.float32(p))
+    if not 0.0 <= p32 < 1.0:
         raise ValueError("dropout probability must be in [0, 1)")
-    return min(255, int(np.floor(256.0 * p + 0.5)))
+    return min(255, int(np.floor(256.0 * p32 + 0.5)))
+
+
+def keep_scale(p: float) -> float:
+    """1 / keep probability = 256 / (256 - t): the factor on kept probabilities."""
+    return 256.0 / (256 - dropout_threshold(p))
 
 
 def _check_key(seed: int, offset: int):
@@ -125,7 +135,7 @@ def head_backward_dropout(q, k, v, dout, scale, causal, kv_len_b, z, keep_scale)
 def _masks(B, H, N, p, seed, offset):
     t = dropout_threshold(p)
     return [[random_bytes(N, N, b * H + h, seed, offset) >= t for h in range(H)]
-            for b in range(B)], 256.0 / (256 - t)
+            for b in range(B)], keep_scale(p)
 
 
 def attention_forward_dropout(q, k, v, scale, causal=False, kv_len=None, p=0.0, seed=0,

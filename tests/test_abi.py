@@ -31,7 +31,7 @@ def lib():
 
 def test_header_declares_the_api():
     assert declared_symbols() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_sparse", "fa_bwd_stage",
-                                  "fa_bwd_workspace_size",
+                                  "fa_bwd_workspace_size", "fa_dropout_threshold",
                                   "fa_fwd", "fa_fwd_deferred", "fa_fwd_dropout", "fa_fwd_partial",
                                   "fa_fwd_sparse",
                                   "fa_last_error", "fa_merge", "fa_split_count",
@@ -308,3 +308,21 @@ def test_deferred_rejects_before_launch(lib, N, dtype, q, code):
     st = lib.fa_fwd_deferred(q, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x700000, 1, 1,
                              N, 64, 0.125, 0, dtype, None, None)
     assert st == code
+
+
+def test_dropout_threshold_matches_the_oracle(lib):
+    """The library's byte threshold (what the kernels receive) equals the oracle's on a
+    grid of p and on the float32 values around every halfway point 256 p = k + 1/2, and
+    rejects p outside [0, 1)."""
+    import numpy as np
+    import oracle
+    ps = [float(x) for x in np.linspace(0.0, 0.9999, 4001)]
+    for k in range(256):
+        mid = np.float32((k + 0.5) / 256)
+        ps += [float(mid), float(np.nextafter(mid, np.float32(0))),
+               float(np.nextafter(mid, np.float32(1)))]
+    ps = [p for p in ps if float(np.float32(p)) < 1.0]
+    for p in ps:
+        assert fa.fa_dropout_threshold(p) == oracle.dropout_threshold(p), p
+    for bad in (-1e-9, 1.0, 2.0, float("nan"), float("inf")):
+        assert fa.fa_dropout_threshold(bad) == -1

@@ -184,3 +184,86 @@ def test_transposed_mask_is_caught(monkeypatch, rocrand_block):
     b = DR.random_bytes(40, 40, 1, 5, 6)
     assert any(b[i, j] != _byte(rocrand_block, i, j, 1, 5, 6) for i, j in ((3, 17), (3, 9),
                                                                           (30, 2)))
+
+
+# ---- the quantisation of p --------------------------------------------------------------
+
+_GOLDEN = os.path.join(_HERE, "golden", "dropout_threshold_cases.json")
+
+
+def _golden_cases():
+    import json
+    return json.load(open(_GOLDEN))["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: repr(c["p"]))
+def test_threshold_golden(case):
+    """Hand-derived thresholds and keep scales (tests/golden/dropout_threshold_cases.json)."""
+    from fractions import Fraction
+    assert DR.dropout_threshold(case["p"]) == case["t"]
+    num, den = case["keep_scale"]
+    assert DR.keep_scale(case["p"]) == float(Fraction(num, den))
+
+
+def _nearest_threshold(p):
+    """Brute force over every byte threshold: the t whose keep probability (256 - t)/256
+    is nearest to 1 - p (the larger t on a tie), p taken as float32."""
+    from fractions import Fraction
+    p = Fraction(float(np.float32(p)))
+    best = None
+    for t in range(256):
+        err = abs(Fraction(256 - t, 256) - (1 - p))
+        if best is None or err < best[0] or err == best[0]:
+            best = (err, t)
+    return best[1]
+
+
+def test_threshold_is_the_nearest_keep_probability():
+    """Over a grid of p and every float32 around each halfway point k + 1/2 of 256 p, the
+    oracle's t is the threshold whose keep probability is nearest 1 - p, within half a
+    grid step; the keep scale is the inverse of the keep probability (their product is 1
+    up to the float64 rounding of the scale)."""
+    from fractions import Fraction
+    ps = list(np.linspace(0.0, 0.999, 1999))
+    for k in range(0, 256):
+        mid = np.float32((k + 0.5) / 256)
+        ps += [float(mid), float(np.nextafter(mid, np.float32(0))),
+               float(np.nextafter(mid, np.float32(1)))]
+    ps = [p for p in ps if 0.0 <= float(np.float32(p)) < 1.0]
+    for p in ps:
+        t = DR.dropout_threshold(p)
+        assert t == _nearest_threshold(p), p
+        keep = Fraction(256 - t, 256)
+        if t < 255:   # the cap at 255 is the only place the error may exceed half a step
+            assert abs(keep - (1 - Fraction(float(np.float32(p))))) <= Fraction(1, 512), p
+        # the keep scale is the inverse keep probability, correctly rounded to float64
+        assert DR.keep_scale(p) == float(1 / keep), p
+        assert abs(Fraction(DR.keep_scale(p)) * keep - 1) <= Fraction(1, 2**52), p
+
+
+_THRESHOLD_MUTANTS = {
+    "round_255p": (lambda p: min(255, int(np.floor(255.0 * float(np.float32(p)) + 0.5))),
+                   DR.keep_scale),
+    "floor_256p": (lambda p: min(255, int(np.floor(256.0 * float(np.float32(p))))),
+                   DR.keep_scale),
+    "inverse_1_minus_p": (DR.dropout_threshold, lambda p: 1.0 / (1.0 - p)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_THRESHOLD_MUTANTS))
+def test_threshold_mutants_are_caught(monkeypatch, name):
+    """A plausible other reading of the quantisation fails one of the pins above."""
+    thr, ks = _THRESHOLD_MUTANTS[name]
+    monkeypatch.setattr(DR, "dropout_threshold", thr)
+    monkeypatch.setattr(DR, "keep_scale", ks)
+    failed = False
+    for case in _golden_cases():
+        try:
+            test_threshold_golden(case)
+        except AssertionError:
+            failed = True
+    try:
+        test_threshold_is_the_nearest_keep_probability()
+    except AssertionError:
+        failed = True
+    assert failed, name
