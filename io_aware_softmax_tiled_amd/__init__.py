@@ -7,7 +7,8 @@ the library's HIP kernels; there is no CPU or PyTorch fallback, and importing a
 function here fails loudly when the library has not been built
 (python -m io_aware_softmax_tiled_amd.build).
 
-Functions have the C entry points' names:
+Functions have the C entry points' names (fwd and bwd are short names of fa_fwd and
+fa_bwd):
     fa_fwd(q, k, v, *, causal=False, scale=None, kv_len=None) -> (o, lse)
     fa_bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, kv_len=None) -> (dq, dk, dv)
     fa_bwd_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, workspace, *, ...) -> None
@@ -21,7 +22,9 @@ Functions have the C entry points' names:
     fa_status_str(code) -> str, fa_last_error() -> str, fa_version() -> int
 Tensors are [B, H, N, d] contiguous (q, k, v, dout: float32, bfloat16 or float16;
 o, dq, dk, dv: float32), lse is [B, H, N] float32, kv_len an int32 [B] device tensor
-or None. The default scale is 1/sqrt(d).
+or None. The default scale is 1/sqrt(d). Caller-supplied buffers (out=, lse=, o, lse,
+dout, dq/dk/dv, workspace) are checked for shape, dtype, device and contiguity before
+any pointer reaches the library.
 """
 from __future__ import annotations
 
@@ -31,7 +34,7 @@ import os
 
 import torch
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_split_count", "fa_fwd_partial",
+__all__ = ["fwd", "bwd", "fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_split_count", "fa_fwd_partial",
            "fa_merge", "fa_fwd_sparse", "fa_bwd_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
            "fa_fwd_deferred", "fa_dropout_threshold", "FA_DEFERRED_MAX_N", "FA_SPARSE_BLOCK", "fa_status_str", "fa_last_error", "fa_version", "FaError", "lib_path",
            "load_library",
@@ -170,6 +173,50 @@ def _kv(kv_len, B, device):
     return kv_len.contiguous()
 
 
+def _expect(t, name, shape, dtype, device):
+    """Check a caller-supplied tensor against what the kernels will read or write through
+    its pointer: exact shape, dtype, device and a contiguous layout. Every size the C
+    layer uses is derived from B, H, N and d, so a buffer that does not match would be
+    read or written out of bounds."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _out(t, name, shape, device):
+    """A float32 output buffer: allocated when t is None, else checked."""
+    if t is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    return _expect(t, name, shape, torch.float32, device)
+
+
+def _workspace(ws, B, H, N, d, device):
+    need = fa_bwd_workspace_size(B, H, N, d)
+    if ws is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes, got {ws.numel() * ws.element_size()}")
+    return ws
+
+
+def _grad_inputs(q, o, dout, lse):
+    """o and lse as fa_fwd returned them, dout like q."""
+    B, H, N, d = (int(x) for x in q.shape)
+    _expect(o, "o", (B, H, N, d), torch.float32, q.device)
+    _expect(lse, "lse", (B, H, N), torch.float32, q.device)
+    _expect(dout, "dout", (B, H, N, d), q.dtype, q.device)
+
+
 def _stream(device, stream):
     s = torch.cuda.current_stream(device) if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -181,8 +228,8 @@ def fa_fwd(q, k, v, *, causal=False, scale=None, kv_len=None, out=None, lse=None
     B, H, N, d = _shape(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     kv = _kv(kv_len, B, q.device)
-    o = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if out is None else out
-    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = _out(out, "out", (B, H, N, d), q.device)
+    lse_t = _out(lse, "lse", (B, H, N), q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d, scale,
@@ -196,15 +243,10 @@ def fa_bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, kv_len=None, work
            stream=None):
     """Backward pass of sum(dout * O): returns (dq, dk, dv), float32 [B,H,N,d]."""
     B, H, N, d = _shape(q, k, v)
-    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
-        raise ValueError("dout must match q in shape and dtype and be contiguous")
-    if o.dtype != torch.float32 or lse.dtype != torch.float32:
-        raise ValueError("o and lse must be the float32 outputs of fa_fwd")
+    _grad_inputs(q, o, dout, lse)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     kv = _kv(kv_len, B, q.device)
-    ws_bytes = fa_bwd_workspace_size(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, B, H, N, d, q.device)
     dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
     dk = torch.empty_like(dq)
     dv = torch.empty_like(dq)
@@ -225,6 +267,10 @@ def fa_bwd_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, workspace, *, causal=
     into the workspace, 1 writes dk and dv (needs D), 2 writes dq (forms its own D),
     3 writes dq and D (fa_bwd is stage 3 then stage 1)."""
     B, H, N, d = _shape(q, k, v)
+    _grad_inputs(q, o, dout, lse)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _expect(t, name, (B, H, N, d), torch.float32, q.device)
+    workspace = _workspace(workspace, B, H, N, d, q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     kv = _kv(kv_len, B, q.device)
     lib = load_library()
@@ -248,10 +294,8 @@ def fa_fwd_partial(q, k, v, *, split_len, causal=False, scale=None, kv_len=None,
     P = fa_split_count(N, int(split_len))
     if P < 0:
         raise ValueError(f"split_len must be a positive multiple of 64 (got {split_len})")
-    o = (torch.empty((P, B, H, N, d), dtype=torch.float32, device=q.device)
-         if out is None else out)
-    lse_t = (torch.empty((P, B, H, N), dtype=torch.float32, device=q.device)
-             if lse is None else lse)
+    o = _out(out, "out", (P, B, H, N, d), q.device)
+    lse_t = _out(lse, "lse", (P, B, H, N), q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.fa_fwd_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
@@ -271,10 +315,8 @@ def fa_merge(o_part, lse_part, *, out=None, lse=None, stream=None):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("partials must be contiguous GPU tensors")
     P, B, H, N, d = (int(x) for x in o_part.shape)
-    o = (torch.empty((B, H, N, d), dtype=torch.float32, device=o_part.device)
-         if out is None else out)
-    lse_t = (torch.empty((B, H, N), dtype=torch.float32, device=o_part.device)
-             if lse is None else lse)
+    o = _out(out, "out", (B, H, N, d), o_part.device)
+    lse_t = _out(lse, "lse", (B, H, N), o_part.device)
     lib = load_library()
     with torch.cuda.device(o_part.device):
         st = lib.fa_merge(_ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse_t), P, B, H, N, d,
@@ -300,8 +342,8 @@ def fa_fwd_sparse(q, k, v, block_mask, *, causal=False, scale=None, kv_len=None,
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     kv = _kv(kv_len, B, q.device)
     bm = _mask(block_mask, N, q.device)
-    o = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if out is None else out
-    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = _out(out, "out", (B, H, N, d), q.device)
+    lse_t = _out(lse, "lse", (B, H, N), q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.fa_fwd_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
@@ -315,16 +357,11 @@ def fa_bwd_sparse(q, k, v, o, dout, lse, block_mask, *, causal=False, scale=None
                   kv_len=None, workspace=None, stream=None):
     """Block-sparse backward of sum(dout * O): returns (dq, dk, dv), float32 [B,H,N,d]."""
     B, H, N, d = _shape(q, k, v)
-    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
-        raise ValueError("dout must match q in shape and dtype and be contiguous")
-    if o.dtype != torch.float32 or lse.dtype != torch.float32:
-        raise ValueError("o and lse must be the float32 outputs of fa_fwd_sparse")
+    _grad_inputs(q, o, dout, lse)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     kv = _kv(kv_len, B, q.device)
     bm = _mask(block_mask, N, q.device)
-    ws_bytes = fa_bwd_workspace_size(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, B, H, N, d, q.device)
     dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
     dk = torch.empty_like(dq)
     dv = torch.empty_like(dq)
@@ -355,8 +392,8 @@ def fa_fwd_dropout(q, k, v, *, p, seed, offset=0, causal=False, scale=None, kv_l
     B, H, N, d = _shape(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     kv = _kv(kv_len, B, q.device)
-    o = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if out is None else out
-    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = _out(out, "out", (B, H, N, d), q.device)
+    lse_t = _out(lse, "lse", (B, H, N), q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
@@ -372,15 +409,10 @@ def fa_bwd_dropout(q, k, v, o, dout, lse, *, p, seed, offset=0, causal=False, sc
     (the mask is regenerated, not stored): returns (dq, dk, dv), float32 [B,H,N,d]."""
     seed, offset = _key(seed, offset)
     B, H, N, d = _shape(q, k, v)
-    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
-        raise ValueError("dout must match q in shape and dtype and be contiguous")
-    if o.dtype != torch.float32 or lse.dtype != torch.float32:
-        raise ValueError("o and lse must be the float32 outputs of fa_fwd_dropout")
+    _grad_inputs(q, o, dout, lse)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     kv = _kv(kv_len, B, q.device)
-    ws_bytes = fa_bwd_workspace_size(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, B, H, N, d, q.device)
     dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
     dk = torch.empty_like(dq)
     dv = torch.empty_like(dq)
@@ -403,8 +435,8 @@ def fa_fwd_deferred(q, k, v, *, causal=False, scale=None, kv_len=None, out=None,
     B, H, N, d = _shape(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     kv = _kv(kv_len, B, q.device)
-    o = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if out is None else out
-    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = _out(out, "out", (B, H, N, d), q.device)
+    lse_t = _out(lse, "lse", (B, H, N), q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.fa_fwd_deferred(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
@@ -412,3 +444,10 @@ def fa_fwd_deferred(q, k, v, *, causal=False, scale=None, kv_len=None, out=None,
                                  _stream(q.device, stream))
     _check(st)
     return o, lse_t
+
+
+# The Python surface under the short names: fwd(q, k, v, *, causal, scale=None,
+# kv_len=None) -> (o, lse) and bwd(q, k, v, o, dout, lse, *, causal, scale=None,
+# kv_len=None) -> (dq, dk, dv), the same functions as fa_fwd and fa_bwd.
+fwd = fa_fwd
+bwd = fa_bwd
