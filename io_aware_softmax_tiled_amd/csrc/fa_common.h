@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_index.h"
+
 namespace fa {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -81,26 +83,6 @@ template <> __device__ inline u32x4 to_f16x8<BF16>(u32x4 x) {
           bf16x2_to_f16x2(x[3])};
 }
 
-// swap bits 2 and 3 of a row index in [0, 32): reading A-operand rows in this order
-// makes accumulator register r of lane l hold row 16*(r/8) + 8*(l/32) + r%8, i.e. each
-// lane's 8 consecutive registers cover 8 consecutive rows
-__device__ inline int kappa(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
-
-// blockIdx.x -> (head, block), block index `slot / heads_per_xcd` counted from 0. When
-// B*H is a multiple of 8 (heads_per_xcd = B*H/8) the mapping is XCD-major: consecutive
-// workgroups go to consecutive XCDs, and all blocks of a head land on one XCD so its
-// K/V tiles are shared in that XCD's L2. Otherwise (heads_per_xcd = 0) heads vary
-// fastest, so every XCD still gets an equal share of the work when there are fewer
-// heads than XCDs or they do not divide evenly. Either way the grid is B*H x blocks.
-struct WgPos {
-  int bh, blk;
-};
-__device__ inline WgPos wg_position(int heads_per_xcd, int w, int BH) {
-  if (heads_per_xcd == 0) return {w % BH, w / BH};
-  const int xcd = w & 7;
-  const int slot = w >> 3;
-  return {(slot % heads_per_xcd) * 8 + xcd, slot / heads_per_xcd};
-}
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
@@ -179,20 +161,5 @@ __device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t offset)
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)offset, 0, 0);
 }
 
-// XOR swizzle of 16-byte chunks inside a 16-bit-element tile row, so that
-// (a) 16 consecutive rows read at one logical chunk hit 16 distinct chunk slots and
-// (b) 4 consecutive rows read through the transposing load hit distinct 64-byte groups.
-template <int D> __device__ __host__ constexpr int chunk_swizzle(int row) {
-  if constexpr (D == 128) {
-    return ((row & 3) << 2) | ((row >> 2) & 3);
-  } else {
-    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-  }
-}
-
-// byte offset of (row, logical 16-byte chunk) in a swizzled [rows][D] 16-bit tile
-template <int D> __device__ __host__ constexpr int tile_off(int row, int chunk) {
-  return row * (D * 2) + ((chunk ^ chunk_swizzle<D>(row)) << 4);
-}
 
 }  // namespace fa

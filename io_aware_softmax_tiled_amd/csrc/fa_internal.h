@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "fa_index.h"
+
 namespace fa {
 
 // block-sparse mask geometry shared by the kernels: 128 x 128 blocks, at most 2048 per
@@ -46,9 +48,6 @@ struct FwdGrid {
 };
 
 FwdGrid fwd_grid(int B, int H, int N, int waves);
-// heads_per_xcd argument of the kernels: B*H/8 when B*H is a multiple of 8 (XCD-major
-// placement), else 0 (heads vary fastest); the grid is B*H x blocks per head either way
-inline int heads_per_xcd(int BH) { return BH % 8 == 0 ? BH / 8 : 0; }
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // forward with the P V product deferred to the end of each query block's key row
 // (bf16/f16, d in {64, 128}, N <= kDeferredMaxN); split, block mask and dropout unused
