@@ -7,10 +7,13 @@ generator and resident in HBM before timing). The metric is attention TFLOP/s un
 the nominal count 4*B*H*N^2*d (halved when causal) for the forward pass plus 2.5x
 that for the backward pass, against the dense bf16 matrix-core peak.
 
-Prints ONE JSON line with the throughput, the roofline of the dominant kernel (each
-kernel of the step timed with HIP events on the stream it runs on: fa_bwd is run as its
-two stages, dQ with D and then dK/dV) and the CPU oracle's throughput on a bounded
-sample of the same workload.
+Prints ONE JSON line with the throughput, the roofline of the dominant kernel and of
+the forward kernel (each kernel of the step timed with HIP events on the stream it runs
+on: fa_bwd is run as its two stages, dQ with D and then dK/dV), per-pass median and
+minimum times (from the timed steps, and from each pass run alone for at least 200 ms),
+and the CPU oracle's throughput on a bounded sample of the same workload. The W warmup
+steps are followed by WARM_S seconds of continuous work so that the timed steps run at
+the sustained clock.
 
   python bench.py [--steps K (100)] [--warmup W (200)] [--gpus 1] [--sweep] [--split-kv] [--sparse]
                   [--dropout] [--deferred] [--configs] [--no-cpu-baseline]
@@ -21,6 +24,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -80,10 +84,45 @@ def cpu_baseline(inp, w, budget_heads=None):
         "value": round(per_head * nheads / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": min(workers, nheads),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{nheads} of {w.B * w.H} heads of the same workload, forward + backward, "
                   f"float64 numpy, {dt:.1f} s wall",
     }
+
+
+def pass_protocol(fa, torch, w, dev, ws, min_ms=200.0, min_calls=20):
+    """Each pass on its own, called back to back until at least min_calls calls and
+    min_ms of timed work, one HIP event pair per call on the stream the kernels run on:
+    median and minimum per call. The forward pass is fa_fwd; the backward pass is the
+    whole fa_bwd (both kernels), on O and LSE from a previous forward call."""
+    stream = torch.cuda.current_stream()
+    fwd = lambda: fa.fa_fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale,
+                            out=dev["o"], lse=dev["lse"])
+    fwd()
+    bwd = lambda: fa.fa_bwd(dev["q"], dev["k"], dev["v"], dev["o"], dev["dout"], dev["lse"],
+                            causal=w.causal, scale=w.scale, workspace=ws)
+    out = {}
+    for name, fn, flops in (("fwd", fwd, w.fwd_flops()), ("bwd", bwd, w.bwd_flops())):
+        times, total = [], 0.0
+        for _ in range(3):
+            fn()
+        while len(times) < min_calls or total < min_ms:
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
+            evs[0].record(stream)
+            for i in range(20):
+                fn()
+                evs[i + 1].record(stream)
+            torch.cuda.synchronize()
+            batch = [evs[i].elapsed_time(evs[i + 1]) for i in range(20)]
+            times += batch
+            total += sum(batch)
+        med = statistics.median(times)
+        out[name] = {"calls": len(times), "timed_ms": round(total, 2),
+                     "median_ms": round(med, 4), "min_ms": round(min(times), 4),
+                     "median_tflops": round(flops / (med * 1e-3) / 1e12, 2),
+                     "median_pct_peak": round(100 * flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    return out
 
 
 # fa_bwd's kernels as fa_bwd_stage calls: stage 3 (dQ, forming and writing D), then
@@ -114,9 +153,21 @@ KERNELS = [("fwd_kernel_16", 1.0), ("bwd_dq_kernel", 1.5), ("bwd_dkdv_kernel", 2
 # The GPU reaches its sustained clock only after tens of milliseconds of continuous
 # work (measured: with 5 warmup steps the bench step ran at 607-611 TFLOP/s, after 50 or
 # more at 686-694), and the inputs are drawn on the host first, so the device starts
-# idle. The default warmup therefore runs long enough to reach the sustained clock, and
-# the supplementary per-shape timings warm each shape up for WARM_S seconds of work.
-WARM_S = 0.2
+# idle. Every timed region, the headline's included whatever --warmup is, is therefore
+# preceded by WARM_S seconds of continuous work on the same shape.
+WARM_S = 0.25
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def bench_workload(fa, torch, w, inp, steps, warmup, warm_s=0.0):
@@ -145,11 +196,15 @@ def bench_workload(fa, torch, w, inp, steps, warmup, warm_s=0.0):
         run_step(fa, dev, w, ws, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_kernel = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
-                  for j in range(len(KERNELS))]
+    samples = [[e[j].elapsed_time(e[j + 1]) for e in evs] for j in range(len(KERNELS))]
+    per_kernel = [sum(x) / steps for x in samples]
     fwd_ms = per_kernel[0]
     bwd_ms = sum(per_kernel[1:])
-    return wall * 1e3 / steps, fwd_ms, bwd_ms, per_kernel
+    stats = {"kernels": [(statistics.median(x), min(x)) for x in samples],
+             "fwd": (statistics.median(samples[0]), min(samples[0])),
+             "bwd": (statistics.median([sum(t) for t in zip(*samples[1:])]),
+                     min(sum(t) for t in zip(*samples[1:])))}
+    return wall * 1e3 / steps, fwd_ms, bwd_ms, per_kernel, stats, dev, ws
 
 
 def main():
@@ -206,16 +261,17 @@ def main():
         del src, dst
     w = workloads.WORKLOADS[WORKLOAD_ID]
     inp = workloads.draw(w)
-    ms_step, fwd_ms, bwd_ms, per_kernel = bench_workload(fa, torch, w, inp, args.steps,
-                                                          args.warmup)
+    ms_step, fwd_ms, bwd_ms, per_kernel, stats, dev, ws = bench_workload(
+        fa, torch, w, inp, args.steps, args.warmup, warm_s=WARM_S)
+    protocol = pass_protocol(fa, torch, w, dev, ws)
 
     fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
     value = (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
     fwd_tf = fwd_f / (fwd_ms * 1e-3) / 1e12
     bwd_tf = bwd_f / (bwd_ms * 1e-3) / 1e12
     kernels = {}
-    for (name, mult), ms in zip(KERNELS, per_kernel):
-        kernels[name] = {"ms": round(ms, 4)}
+    for (name, mult), ms, (med, mn) in zip(KERNELS, per_kernel, stats["kernels"]):
+        kernels[name] = {"ms": round(ms, 4), "median_ms": round(med, 4), "min_ms": round(mn, 4)}
         if mult:
             kernels[name]["tflops"] = round(mult * fwd_f / (ms * 1e-3) / 1e12, 2)
     # the dominant kernel of the step: the longest average launch, timed live with HIP
@@ -232,6 +288,18 @@ def main():
         "traffic": measured_traffic(name),
         "kernel": name,
         "avg_launch_ms": round(per_kernel[dom], 4),
+    }
+    # the forward kernel's own roofline (the pass the 50%-of-peak target is set on)
+    fwd_achieved = fwd_f / (per_kernel[0] * 1e-3) / 1e12
+    roofline_fwd = {
+        "bound": "mfma",
+        "achieved": round(fwd_achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(fwd_achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": measured_traffic(KERNELS[0][0]),
+        "kernel": KERNELS[0][0],
+        "avg_launch_ms": round(per_kernel[0], 4),
     }
     line = {
         "metric": "attention fwd+bwd TFLOP/s (nominal 4BHN^2d/2 causal fwd + 2.5x bwd) and "
@@ -250,12 +318,17 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "passes": "fwd+bwd"},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "passes": {"fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tf, 2),
+        "warm_s": WARM_S,
+        "passes": {"fwd": {"ms": round(fwd_ms, 4), "median_ms": round(stats["fwd"][0], 4),
+                           "min_ms": round(stats["fwd"][1], 4), "tflops": round(fwd_tf, 2),
                            "pct_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2)},
-                   "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 2),
+                   "bwd": {"ms": round(bwd_ms, 4), "median_ms": round(stats["bwd"][0], 4),
+                           "min_ms": round(stats["bwd"][1], 4), "tflops": round(bwd_tf, 2),
                            "pct_peak": round(100 * bwd_tf / PEAK_BF16_TFLOPS, 2)}},
+        "pass_protocol": protocol,
         "kernels": kernels,
         "roofline": roofline,
+        "roofline_fwd": roofline_fwd,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(inp, w),
     }
     print(json.dumps(line), flush=True)
@@ -281,8 +354,8 @@ def sweep(fa, torch, workloads):
             for N in (512, 1024, 2048, 4096, 8192, 16384):
                 B, H = max(1, 16384 // N), 2048 // d
                 w, inp = workloads.custom(B, H, N, d, "bf16", causal, seed=0)
-                ms_step, fwd_ms, bwd_ms, _ = bench_workload(fa, torch, w, inp, 10, 3,
-                                                            warm_s=WARM_S)
+                ms_step, fwd_ms, bwd_ms, *_ = bench_workload(fa, torch, w, inp, 10, 3,
+                                                             warm_s=WARM_S)
                 print(json.dumps({
                     "sweep": True, "B": B, "H": H, "N": N, "d": d, "causal": causal,
                     "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
