@@ -173,10 +173,13 @@ def _bwd_job(args):
 
 
 def default_workers() -> int:
+    """Worker processes for the per-head pools: the cores this process may run on, at
+    most 16 (a GPU host's CPU share per GPU here, whatever the affinity mask shows)."""
     try:
-        return len(os.sched_getaffinity(0))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def attention_forward_heads(q, k, v, scale, causal=False, kv_len=None, heads=None,
