@@ -83,8 +83,9 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, float* o, float* 
            const int32_t* kv_len, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes (the per-row
- * D_i = sum_k dO_ik O_ik, float32 [B,H,N], rounded up to 256 bytes).
+ * Bytes of device workspace fa_bwd needs for these sizes: the per-row
+ * D_i = sum_k dO_ik O_ik (float32 [B,H,N]) and then the largest |dO| of every group of
+ * 32 query rows (float32 [B,H,ceil(N/32)]), each region rounded up to 256 bytes.
  */
 FA_API size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -96,10 +97,17 @@ FA_API size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  * workspace: device memory of at least fa_bwd_workspace_size(B,H,N,d) bytes,
  * 256-byte aligned, owned by the caller, contents on entry irrelevant.
  * Two kernels run in order on `stream`: dq (queries outer), which also forms
- * D = rowsum(dout*o) for its rows and writes it into the workspace, then dk/dv (keys
- * outer), which reads D; each output is written exactly once, so results are
- * deterministic. dtype must be FA_BF16 or FA_F16 (an FA_F32
+ * D = rowsum(dout*o) for its rows and the 32-row maxima of |dout| and writes them into
+ * the workspace, then dk/dv (keys outer), which reads them; each output is written
+ * exactly once, so results are deterministic. dtype must be FA_BF16 or FA_F16 (an FA_F32
  * backward is not provided: FA_EUNSUPPORTED).
+ * Precision: the matrix-core products run on fp16 operands with fp32 accumulation.
+ * dout is multiplied by a power of two (per query row in the dq kernel, per workgroup
+ * from the 32-row maxima in the dk/dv kernel) that brings its largest magnitude into
+ * [1, 2) before rounding, and the gradients are divided by it exactly at the end, so
+ * the relative precision does not depend on the magnitude of dout. q, k and v are
+ * rounded to fp16 as they are: their magnitudes must stay within the fp16 range
+ * (|x| <= 65504; values below 2^-14 lose relative precision).
  */
 FA_API int fa_bwd(const void* q, const void* k, const void* v, const float* o,
            const void* dout, const float* lse, float* dq, float* dk, float* dv,
@@ -182,9 +190,10 @@ FA_API int fa_bwd_sparse(const void* q, const void* k, const void* v, const floa
 
 /*
  * One stage of the backward pass, into caller-allocated outputs: stage 0 writes
- * D = rowsum(dout * o) into the workspace; stage 1 writes dk and dv (reads D); stage 2
- * writes dq (it forms D for its own rows from dout and o, and reads nothing from the
- * workspace); stage 3 is stage 2 that also writes D into the workspace. fa_bwd is
+ * D = rowsum(dout * o) and the 32-row maxima of |dout| into the workspace; stage 1
+ * writes dk and dv (reads both); stage 2 writes dq (it forms D for its own rows from
+ * dout and o, and reads nothing from the workspace); stage 3 is stage 2 that also writes
+ * D and the maxima into the workspace. fa_bwd is
  * stage 3 then stage 1 on one stream; stages 0, 1, 2 in that order give the same
  * results bit for bit (both ways of forming D sum in the same order). After stage 0,
  * stages 1 and 2 are independent and may run on two streams. Arguments, checks and

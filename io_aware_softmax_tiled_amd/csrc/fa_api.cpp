@@ -346,6 +346,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* o, const 
 
   fa::BwdArgs a{q,  k,  v,  o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal ? 1 : 0,
                 dtype, kv_len, static_cast<float*>(workspace)};
+  a.dmax = reinterpret_cast<float*>(static_cast<char*>(workspace) + fa::bwd_delta_bytes(B, H, N));
   a.block_mask = block_mask;
   a.drop_t = drop.t;
   a.seed = drop.seed;

@@ -49,20 +49,24 @@ template <> __device__ inline float to_f32<F16>(uint16_t x) {
 }
 
 // ---------------------------------------------------------------------------------
-// 1. D = rowsum(dO * O). One thread per 8 elements; D/8 threads per row.
+// 1. D = rowsum(dO * O) and the largest |dO| of every 32-row group. One workgroup per
+//    group of 32 rows of one head, one thread per 8 elements (D/8 threads per row).
 // ---------------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
+__global__ __launch_bounds__(4 * D) void bwd_pre_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ O, float* __restrict__ delta,
-    size_t rows) {
+    float* __restrict__ dmax, int N, int n_groups) {
   constexpr int kTPR = D / 8;
-  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  const size_t row = idx / kTPR;
-  float s = 0.f;
-  if (row < rows) {
-    const u32x4 g = *reinterpret_cast<const u32x4*>(dO + idx * 8);
-    const f32x4 o0 = *reinterpret_cast<const f32x4*>(O + idx * 8);
-    const f32x4 o1 = *reinterpret_cast<const f32x4*>(O + idx * 8 + 4);
+  constexpr int kWaves = 4 * D / 64;
+  __shared__ float wmax[kWaves];
+  const int bh = blockIdx.x / n_groups, grp = blockIdx.x % n_groups;
+  const int r = grp * kDmaxRows + (int)threadIdx.x / kTPR;   // row inside the head
+  const size_t idx = ((size_t)bh * N + r) * D + (threadIdx.x % kTPR) * 8;
+  float s = 0.f, m = 0.f;
+  if (r < N) {
+    const u32x4 g = *reinterpret_cast<const u32x4*>(dO + idx);
+    const f32x4 o0 = *reinterpret_cast<const f32x4*>(O + idx);
+    const f32x4 o1 = *reinterpret_cast<const f32x4*>(O + idx + 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float lo = to_f32<T>((uint16_t)(g[j] & 0xffff));
@@ -72,10 +76,21 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
       s = fmaf(lo, olo, s);
       s = fmaf(hi, ohi, s);
     }
+    m = absmax8<T>(g);
   }
 #pragma unroll
   for (int off = kTPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kTPR);
-  if (row < rows && (threadIdx.x % kTPR) == 0) delta[row] = s;
+  if (r < N && (threadIdx.x % kTPR) == 0) delta[(size_t)bh * N + r] = s;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float mm = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) mm = fmaxf(mm, wmax[w]);
+    dmax[(size_t)bh * n_groups + grp] = mm;
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -93,7 +108,8 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ O, const float* __restrict__ LSE, float* __restrict__ delta,
-    int write_delta, float* __restrict__ dQ, int BH, int H, int N, float scale, float sl2,
+    float* __restrict__ dmax, int write_delta, float* __restrict__ dQ, int BH, int H, int N,
+    float scale, float sl2,
     int causal, const int* __restrict__ kv_len, int n_mblk, int heads_per_xcd,
     const uint8_t* __restrict__ bmask, int n_sb, uint32_t seed_lo, uint32_t seed_hi,
     uint32_t offset, int drop_t, float keep_scale) {
@@ -197,12 +213,14 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(
   // for bit
   u32x4 qf[kKC], of[kKC];
   float dpart[kKC];
+  float dmx = 0.f;  // largest |dO| of this lane's half of the row
 #pragma unroll
   for (int c = 0; c < kKC; ++c) {
     const size_t off = head + (size_t)qrow_c * D + 16 * c + 8 * hh;
     qf[c] = to_f16x8<T>(*reinterpret_cast<const u32x4*>(Q + off));
     const u32x4 g = *reinterpret_cast<const u32x4*>(dO + off);
-    of[c] = to_f16x8<T>(g);
+    of[c] = g;
+    dmx = fmaxf(dmx, absmax8<T>(g));
     const f32x4 o0 = *reinterpret_cast<const f32x4*>(O + off);
     const f32x4 o1 = *reinterpret_cast<const f32x4*>(O + off + 4);
     float sum = 0.f;
@@ -222,8 +240,23 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(
         dpart[c] = t2;
         dpart[c ^ m] = t2;
       }
-  const float dlt = sum_halves(dpart[0]);
-  if (write_delta && hh == 0 && qrow < N) delta[(size_t)bh * N + qrow] = dlt;
+  const float dlt_raw = sum_halves(dpart[0]);
+  if (write_delta && hh == 0 && qrow < N) delta[(size_t)bh * N + qrow] = dlt_raw;
+  // dO of this row is taken times a power of two r that brings its largest magnitude
+  // into [1, 2) before rounding to fp16; dP, D and dS scale with it, and dQ is divided
+  // by r at the end (exact)
+  const float row_max = max_halves(dmx);
+  const float rsc = pow2_scale(row_max);
+#pragma unroll
+  for (int c = 0; c < kKC; ++c) of[c] = to_f16x8_scaled<T>(of[c], rsc);
+  const float dlt = dlt_raw * rsc;
+  if (write_delta) {
+    // the largest |dO| of the wave's 32 rows, for the dK/dV kernel's scale
+    float gm = row_max;
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) gm = fmaxf(gm, __shfl_xor(gm, off, 32));
+    if (lane == 0 && wq0 < N) dmax[(size_t)bh * ((N + kDmaxRows - 1) / kDmaxRows) + wq0 / kDmaxRows] = gm;
+  }
   // a row that sees no key (LSE = -inf, block-sparse) must give P = 0: +inf here
   const float lse_row = LSE[(size_t)bh * N + qrow_c];
   const float lse2 = lse_row == -INFINITY ? INFINITY : lse_row * kLog2e;
@@ -324,15 +357,16 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(
            (FA_LDS uint8_t*)Vb0);
   }
 
-  // dQ = scale * dQ_acc: lane (query, hh), register r <-> d = 32db + 8(r/4) + 4hh + r%4
+  // dQ = scale / r * dQ_acc: lane (query, hh), register r <-> d = 32db + 8(r/4) + 4hh + r%4
   if (qrow < N) {
     float* dqr = dQ + head + (size_t)qrow * D;
+    const float sq = scale / rsc;
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
-        const f32x4 val = {scale * dqacc[db][4 * a4 + 0], scale * dqacc[db][4 * a4 + 1],
-                           scale * dqacc[db][4 * a4 + 2], scale * dqacc[db][4 * a4 + 3]};
+        const f32x4 val = {sq * dqacc[db][4 * a4 + 0], sq * dqacc[db][4 * a4 + 1],
+                           sq * dqacc[db][4 * a4 + 2], sq * dqacc[db][4 * a4 + 3]};
         *reinterpret_cast<f32x4*>(dqr + db * 32 + 8 * a4 + 4 * hh) = val;
       }
   }
@@ -340,17 +374,21 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int B, int H, int N, int d) {
-  (void)d;
+size_t bwd_delta_bytes(int B, int H, int N) {
   const size_t bytes = (size_t)B * H * N * sizeof(float);
   return (bytes + 255) / 256 * 256;
+}
+
+size_t bwd_workspace_bytes(int B, int H, int N, int d) {
+  (void)d;
+  const size_t groups = (size_t)B * H * ((N + kDmaxRows - 1) / kDmaxRows);
+  return bwd_delta_bytes(B, H, N) + (groups * sizeof(float) + 255) / 256 * 256;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages) {
   if (a.dtype == kDtypeF32) return hipErrorNotSupported;  // rejected by the API layer
   const int BH = a.B * a.H;
-  const size_t rows = (size_t)BH * a.N;
-  const int pre_blocks = (int)((rows * (a.d / 8) + kThreads - 1) / kThreads);
+  const int n_groups = (a.N + kDmaxRows - 1) / kDmaxRows;
   const float sl2 = a.scale * kLog2e;
   const int hpx = heads_per_xcd(BH);
   const auto* q16 = static_cast<const uint16_t*>(a.q);
@@ -364,14 +402,15 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages) {
 #define FA_BWD_LAUNCH2(TAG, DIM, SP, DR)                                                     \
   do {                                                                                       \
     if (stages & 1)                                                                          \
-      hipLaunchKernelGGL((bwd_pre_kernel<TAG, DIM>), dim3(pre_blocks), dim3(kThreads), 0,    \
-                         stream, dO16, a.o, a.delta, rows);                                  \
+      hipLaunchKernelGGL((bwd_pre_kernel<TAG, DIM>), dim3(BH * n_groups), dim3(4 * DIM), 0,  \
+                         stream, dO16, a.o, a.delta, a.dmax, a.N, n_groups);                  \
     if (stages & 4) {                                                                        \
       constexpr int kW = (DIM == 128 && !SP) ? 8 : 4;                                        \
       const int n_mblk = (a.N + 32 * kW - 1) / (32 * kW);                                    \
       hipLaunchKernelGGL((bwd_dq_kernel<TAG, DIM, kW, SP, DR>), dim3(BH * n_mblk),            \
                          dim3(64 * kW), 0, stream, q16, k16, v16, dO16, a.o, a.lse, a.delta,  \
-                         (stages & 8) ? 1 : 0, a.dq, BH, a.H, a.N, a.scale, sl2, a.causal,    \
+                         a.dmax, (stages & 8) ? 1 : 0, a.dq, BH, a.H, a.N, a.scale, sl2,      \
+                         a.causal,                                                            \
                          a.kv_len, n_mblk, hpx, a.block_mask, n_sb, seed_lo, seed_hi,         \
                          a.offset, a.drop_t, keep_scale);                                     \
     }                                                                                        \

@@ -40,7 +40,8 @@ template <typename T, int D, bool kSparse, bool kDropout>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ delta, float* __restrict__ dK,
+    const float* __restrict__ LSE, const float* __restrict__ delta,
+    const float* __restrict__ dmax, float* __restrict__ dK,
     float* __restrict__ dV, int BH, int H, int N, float scale, float sl2, int causal,
     const int* __restrict__ kv_len, int n_kblk, int heads_per_xcd,
     const uint8_t* __restrict__ bmask, int n_sb, uint32_t seed_lo, uint32_t seed_hi,
@@ -114,6 +115,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     __syncthreads();
     nt = tlist_len;
   }
+  // dO is taken times a power of two sc that brings the largest |dO| of the query rows
+  // this workgroup visits (from the 32-row maxima the D pass wrote) into [1, 2) before it
+  // is rounded to fp16; dP, D, dS and both accumulators scale with it, and the epilogue
+  // divides by sc (exact). Every wave forms the same value.
+  float sc;
+  {
+    const int ng = (N + kDmaxRows - 1) / kDmaxRows;
+    const float* mp = dmax + (size_t)bh * ng;
+    float m = 0.f;
+    for (int gi2 = i0 * (kBQ / kDmaxRows) + lane; gi2 < ng; gi2 += 64) m = fmaxf(m, mp[gi2]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    sc = pow2_scale(m);
+  }
   auto tile_at = [&](int s) {
     if constexpr (kSparse) return __builtin_amdgcn_readfirstlane((int)tlist[s]);
     else return i0 + s;
@@ -154,11 +169,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       const int ci = tid + kThreads * j;
       const int row = ci / kCPR, ch = ci % kCPR;
       lds_write16(qb + tile_off<D>(row, ch), to_f16x8<T>(qs[j]));
-      lds_write16(ob + tile_off<D>(row, ch), to_f16x8<T>(os[j]));
+      lds_write16(ob + tile_off<D>(row, ch), to_f16x8_scaled<T>(os[j], sc));
     }
     if (tid < kBQ) {
       st[tid] = s_lse;
-      st[kBQ + tid] = s_dlt;
+      st[kBQ + tid] = s_dlt * sc;
     }
   };
 
@@ -385,9 +400,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int d0 = 32 * db + 8 * a4 + 4 * hh;
-        const f32x4 kk = {scale * dkacc[db][4 * a4], scale * dkacc[db][4 * a4 + 1],
-                          scale * dkacc[db][4 * a4 + 2], scale * dkacc[db][4 * a4 + 3]};
-        const float vs = kDropout ? keep_scale : 1.0f;
+        const float ks = scale / sc;
+        const f32x4 kk = {ks * dkacc[db][4 * a4], ks * dkacc[db][4 * a4 + 1],
+                          ks * dkacc[db][4 * a4 + 2], ks * dkacc[db][4 * a4 + 3]};
+        const float vs = (kDropout ? keep_scale : 1.0f) / sc;
         const f32x4 vv = {vs * dvacc[db][4 * a4], vs * dvacc[db][4 * a4 + 1],
                           vs * dvacc[db][4 * a4 + 2], vs * dvacc[db][4 * a4 + 3]};
         *reinterpret_cast<f32x4*>(dkr + d0) = kk;
@@ -414,7 +430,8 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   const uint32_t seed_lo = (uint32_t)a.seed, seed_hi = (uint32_t)(a.seed >> 32);
 #define FA_DKDV_LAUNCH2(TAG, DIM, SP, DR)                                                    \
   hipLaunchKernelGGL((bwd_dkdv_kernel<TAG, DIM, SP, DR>), dim3(BH * n_kblk), dim3(kThreads), \
-                     0, stream, q16, k16, v16, dO16, a.lse, a.delta, a.dk, a.dv, BH, a.H,    \
+                     0, stream, q16, k16, v16, dO16, a.lse, a.delta, a.dmax, a.dk, a.dv, BH, \
+                     a.H,                                                                     \
                      a.N, a.scale, sl2, a.causal, a.kv_len, n_kblk, hpx, a.block_mask, n_sb, \
                      seed_lo, seed_hi, a.offset, a.drop_t, keep_scale)
 #define FA_DKDV_LAUNCH(TAG, DIM)                                              \

@@ -83,6 +83,58 @@ template <> __device__ inline u32x4 to_f16x8<BF16>(u32x4 x) {
           bf16x2_to_f16x2(x[3])};
 }
 
+// the two elements of a packed bf16 or f16 pair as fp32
+template <typename T> __device__ inline void unpack2(uint32_t x, float& lo, float& hi);
+template <> __device__ inline void unpack2<BF16>(uint32_t x, float& lo, float& hi) {
+  lo = __uint_as_float(x << 16);
+  hi = __uint_as_float(x & 0xffff0000u);
+}
+template <> __device__ inline void unpack2<F16>(uint32_t x, float& lo, float& hi) {
+  const f16x2 v = __builtin_bit_cast(f16x2, x);
+  lo = (float)v[0];
+  hi = (float)v[1];
+}
+
+// 8 input elements -> 8 fp16 of x * s, s a power of two (exact unless the product
+// leaves the fp16 range)
+template <typename T> __device__ inline u32x4 to_f16x8_scaled(u32x4 x, float s) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo, hi;
+    unpack2<T>(x[i], lo, hi);
+    r[i] = Mfma<F16>::pack(lo * s, hi * s);
+  }
+  return r;
+}
+
+// largest magnitude among the 8 elements of a 16-bit chunk, as fp32 (for non-NaN bf16
+// and fp16 the magnitude bits order like unsigned integers)
+template <typename T> __device__ inline float absmax8(u32x4 x) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = x[i] & 0x7fff7fffu;
+    m = max(m, max(a & 0xffffu, a >> 16));
+  }
+  float lo, hi;
+  unpack2<T>(m, lo, hi);
+  return lo;
+}
+
+// Power-of-two scale that brings a magnitude m into [1, 2): 2^(1 - e) for m = f 2^e,
+// f in [0.5, 1), the exponent clamped so the scale stays a normal fp32; 1 for m = 0 or a
+// non-finite m. The backward pass multiplies dO by it before rounding to fp16, so dO,
+// dP and dS keep fp16's 11-bit precision whatever the magnitude of the gradient (the
+// scale is undone exactly in the fp32 epilogue).
+__device__ inline float pow2_scale(float m) {
+  if (!(m > 0.f) || !(m <= 3.4e38f)) return 1.0f;
+  int e;
+  (void)__builtin_frexpf(m, &e);
+  const int x = min(126, max(-126, 1 - e));
+  return __builtin_ldexpf(1.0f, x);
+}
+
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float log2_fast(float x) { return __builtin_amdgcn_logf(x); }

@@ -70,12 +70,19 @@ struct BwdArgs {
   int dtype;
   const int* kv_len;
   float* delta;  // workspace: D_i = rowsum(dO * O), [B,H,N]
+  // workspace, after D: the largest |dO| of every group of 32 query rows, [B,H,ceil(N/32)]
+  // (each (batch, head) starts a new group); the dK/dV kernel derives its dO scale from it
+  float* dmax = nullptr;
   const uint8_t* block_mask = nullptr;  // block-sparse mask as in FwdArgs, or nullptr
   int drop_t = -1;                      // dropout as in FwdArgs
   uint64_t seed = 0;
   uint32_t offset = 0;
 };
 
+// the workspace: D ([B,H,N] floats) then the dO maxima ([B,H,ceil(N/32)] floats), each
+// region starting on a 256-byte boundary
+constexpr int kDmaxRows = 32;
+size_t bwd_delta_bytes(int B, int H, int N);
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
 
 struct MergeArgs {

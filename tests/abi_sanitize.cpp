@@ -25,10 +25,14 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t) { ++g_fwd_calls; g_last_fwd
 hipError_t launch_fwd_deferred(const FwdArgs& a, hipStream_t) { ++g_fwd_calls; g_last_fwd = a; return g_launch_result; }
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t, int stages) { ++g_bwd_calls; g_last_bwd = a; g_bwd_stages = stages; return g_launch_result; }
 hipError_t launch_merge(const MergeArgs&, hipStream_t) { ++g_merge_calls; return g_launch_result; }
-size_t bwd_workspace_bytes(int B, int H, int N, int d) {
-  (void)d;
+size_t bwd_delta_bytes(int B, int H, int N) {
   const size_t bytes = (size_t)B * H * N * sizeof(float);
   return (bytes + 255) / 256 * 256;
+}
+size_t bwd_workspace_bytes(int B, int H, int N, int d) {
+  (void)d;
+  const size_t groups = (size_t)B * H * ((N + kDmaxRows - 1) / kDmaxRows);
+  return bwd_delta_bytes(B, H, N) + (groups * sizeof(float) + 255) / 256 * 256;
 }
 }  // namespace fa
 
@@ -105,6 +109,7 @@ static void abi_backward() {
   g_bwd_calls = 0;
   CHECK(call(P(9), ws, FA_BF16, (float*)P(6)) == FA_OK);
   CHECK(g_bwd_calls == 1 && g_last_bwd.delta == (float*)P(9) && g_bwd_stages == fa::kBwdAll);
+  CHECK((char*)g_last_bwd.dmax == P(9) + fa::bwd_delta_bytes(B, H, N) && (uintptr_t)g_last_bwd.dmax % 256 == 0);
   CHECK(call(P(9), ws - 1, FA_BF16, (float*)P(6)) == FA_EWORKSPACE);
   CHECK(call(nullptr, ws, FA_BF16, (float*)P(6)) == FA_EWORKSPACE);
   CHECK(call(P(9) + 128, ws, FA_BF16, (float*)P(6)) == FA_EINVAL);   // 256-byte alignment

@@ -165,3 +165,23 @@ def test_head_counts_not_multiple_of_8(B, H):
     for name, got, ref in (("O", o, ro), ("LSE", lse, rl), ("dQ", dq, rq), ("dK", dk, rk),
                            ("dV", dv, rv)):
         U.compare(name, got, ref, "bf16")
+
+
+@pytest.mark.parametrize("dtype,mult", [("bf16", 2.0 ** -20), ("bf16", 2.0 ** 12),
+                                        ("bf16", 2.0 ** -60), ("f16", 2.0 ** -10)])
+def test_bwd_gradient_magnitude(dtype, mult):
+    """dO scaled by a power of two (exact in the input dtype): the gradients scale by the
+    same factor, so grad / mult must meet the usual tolerance against the oracle's
+    gradients of the same inputs divided by mult. Small dO would otherwise leave the
+    fp16 range of the matrix-core operands (dS, dO) and large dO would overflow dS;
+    peaky rows (Q x 4) over 1000 keys, causal, head_dim 128."""
+    w, inp = workloads.custom(1, 4, 1000, 128, dtype, True, q_mult=4.0, seed=9)
+    inp["dout"] = (inp["dout"].double() * mult).to(workloads.DTYPES[dtype])
+    U.say(f"[bwd] gradient magnitude {dtype} x {mult:g}")
+    o, lse, dq, dk, dv = U.gpu_bwd(inp)
+    ref = U.oracle_bwd(inp)
+    heads = [(0, h) for h in range(4)]
+    rep = {}
+    for name, t, i in (("dQ", dq, 0), ("dK", dk, 1), ("dV", dv, 2)):
+        U.compare(name, _sel(t, heads).double() / mult, _stack(ref, heads, i) / mult, dtype, rep)
+    U.say(f"  errors (relative to the gradient scale) {rep}")
