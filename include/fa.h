@@ -189,6 +189,25 @@ FA_API int fa_bwd_sparse(const void* q, const void* k, const void* v, const floa
                   size_t workspace_bytes, void* stream);
 
 /*
+ * fa_bwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * The scratch fa_bwd keeps in the workspace (D and the 32-row maxima of |dout|) lives in
+ * a statically allocated device array of FA_NOALLOC_SCRATCH_BYTES on every GPU the
+ * library runs on, held until the process ends; the call allocates and frees nothing.
+ * Sizes whose fa_bwd_workspace_size exceeds FA_NOALLOC_SCRATCH_BYTES are rejected with
+ * FA_EWORKSPACE (B*H*N up to about 8.1 million rows fit). Every call on one GPU shares
+ * that GPU's array, whose contents need no clearing (each call writes every element it
+ * reads before reading it): calls that overlap in time on one GPU (two streams, two host
+ * threads) race on it and must be serialised by the caller. Other arguments, outputs,
+ * errors and results are those of fa_bwd, bit for bit.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32 << 20)
+FA_API int fa_bwd_noalloc(const void* q, const void* k, const void* v, const float* o,
+                   const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                   int B, int H, int N, int d, float scale, int causal, int dtype,
+                   const int32_t* kv_len, void* stream);
+
+/*
  * One stage of the backward pass, into caller-allocated outputs: stage 0 writes
  * D = rowsum(dout * o) and the 32-row maxima of |dout| into the workspace; stage 1
  * writes dk and dv (reads both); stage 2 writes dq (it forms D for its own rows from

@@ -34,7 +34,7 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_split_count", "fa_fwd_partial",
+__all__ = ["fwd", "bwd", "fa_fwd", "fa_bwd", "fa_bwd_noalloc", "FA_NOALLOC_SCRATCH_BYTES", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_split_count", "fa_fwd_partial",
            "fa_merge", "fa_fwd_sparse", "fa_bwd_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
            "fa_fwd_deferred", "fa_dropout_threshold", "FA_DEFERRED_MAX_N", "FA_SPARSE_BLOCK", "fa_status_str", "fa_last_error", "fa_version", "FaError", "lib_path",
            "load_library",
@@ -43,6 +43,7 @@ __all__ = ["fwd", "bwd", "fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_s
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_SPARSE_BLOCK = 128
 FA_DEFERRED_MAX_N = 512
+FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 _DTYPE_CODE = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.float16: FA_F16}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -75,6 +76,9 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32,
                            i32, vp, vp, sz, vp]
     lib.fa_bwd.restype = i32
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                   i32, i32, vp, vp]
+    lib.fa_bwd_noalloc.restype = i32
     lib.fa_bwd_stage.argtypes = [i32] + lib.fa_bwd.argtypes
     lib.fa_bwd_stage.restype = i32
     lib.fa_bwd_workspace_size.argtypes = [i32, i32, i32, i32]
@@ -259,6 +263,26 @@ def fa_bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, kv_len=None, work
                         _stream(q.device, stream))
     _check(st)
     return dq, dk, dv
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, *, causal=False, scale=None,
+                   kv_len=None, stream=None):
+    """fa_bwd into caller-allocated dq, dk, dv (float32 [B,H,N,d]) with the library's
+    static per-GPU scratch instead of a workspace: the call allocates nothing. Calls
+    that overlap in time on one GPU race on the scratch."""
+    B, H, N, d = _shape(q, k, v)
+    _grad_inputs(q, o, dout, lse)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _expect(t, name, (B, H, N, d), torch.float32, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    kv = _kv(kv_len, B, q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, scale,
+                                int(bool(causal)), _DTYPE_CODE[q.dtype], _ptr(kv),
+                                _stream(q.device, stream))
+    _check(st)
 
 
 def fa_bwd_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, workspace, *, causal=False,

@@ -27,6 +27,17 @@ int fail(int status, const char* fmt, ...) {
 
 void clear_error() { g_last_error[0] = '\0'; }
 
+}  // namespace
+
+namespace fa {
+int api_fail(int status, const char* msg) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
+  return status;
+}
+}  // namespace fa
+
+namespace {
+
 size_t elem_size(int dtype) { return dtype == FA_F32 ? 4 : 2; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -81,6 +92,18 @@ const char* fa_last_error(void) { return g_last_error; }
 int fa_version(void) { return 100; /* 0.1.0 */ }
 
 }  // extern "C"
+
+namespace fa {
+// the size, dtype and scale checks of the backward entry points, without any pointer
+int bwd_check_sizes(int B, int H, int N, int d, float scale, int dtype) {
+  clear_error();
+  const int st = check_common(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (dtype == FA_F32)
+    return fail(FA_EUNSUPPORTED, "the backward pass takes bf16 or f16 inputs, not f32");
+  return FA_OK;
+}
+}  // namespace fa
 
 extern "C" int fa_dropout_threshold(float p) {
   if (!(p >= 0.0f && p < 1.0f)) return -1;

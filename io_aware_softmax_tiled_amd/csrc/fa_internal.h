@@ -101,4 +101,9 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages = kBwdAll
 // the dK/dV kernel alone (fa_bwd_dkdv.hip; reads the D that bwd_pre wrote)
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 
+// records msg as the thread's last error (fa_last_error) and returns status
+int api_fail(int status, const char* msg);
+// the backward entry points' checks of sizes, dtype and scale (no pointer is looked at)
+int bwd_check_sizes(int B, int H, int N, int d, float scale, int dtype);
+
 }  // namespace fa

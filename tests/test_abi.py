@@ -30,7 +30,8 @@ def lib():
 
 
 def test_header_declares_the_api():
-    assert declared_symbols() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_sparse", "fa_bwd_stage",
+    assert declared_symbols() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_noalloc", "fa_bwd_sparse",
+                                  "fa_bwd_stage",
                                   "fa_bwd_workspace_size", "fa_dropout_threshold",
                                   "fa_fwd", "fa_fwd_deferred", "fa_fwd_dropout", "fa_fwd_partial",
                                   "fa_fwd_sparse",
@@ -329,3 +330,20 @@ def test_dropout_threshold_matches_the_oracle(lib):
         assert fa.fa_dropout_threshold(p) == oracle.dropout_threshold(p), p
     for bad in (-1e-9, 1.0, 2.0, float("nan"), float("inf")):
         assert fa.fa_dropout_threshold(bad) == -1
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """fa_bwd_noalloc refuses, on the host, sizes whose scratch exceeds the static array
+    (no GPU is touched), and validates like fa_bwd."""
+    B, H, N, d = 64, 32, 8192, 64        # 16.8 M rows: beyond the 32 MiB scratch
+    assert fa.fa_bwd_workspace_size(B, H, N, d) > fa.FA_NOALLOC_SCRATCH_BYTES
+    st = lib.fa_bwd_noalloc(P, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x400000,
+                            P + 0x500000, P + 0x600000, P + 0x700000, P + 0x800000, B, H, N, d,
+                            0.125, 0, 1, None, None)
+    assert st == FA_EWORKSPACE and "static scratch" in fa.fa_last_error()
+    st = lib.fa_bwd_noalloc(P, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x400000,
+                            P + 0x500000, P + 0x600000, P + 0x700000, P + 0x800000, 1, 1, 64, 96,
+                            0.125, 0, 1, None, None)
+    assert st == FA_EUNSUPPORTED
+    assert lib.fa_bwd_noalloc(None, None, None, None, None, None, None, None, None, 0, 1, 64, 64,
+                              0.125, 0, 1, None, None) == FA_OK
