@@ -99,9 +99,11 @@ FA_API size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  * Two kernels run in order on `stream`: dq (queries outer), which also forms
  * D = rowsum(dout*o) for its rows and the 32-row maxima of |dout| and writes them into
  * the workspace, then dk/dv (keys outer), which reads them; each output is written
- * exactly once, so results are deterministic. dtype must be FA_BF16 or FA_F16 (an FA_F32
- * backward is not provided: FA_EUNSUPPORTED).
- * Precision: the matrix-core products run on fp16 operands with fp32 accumulation.
+ * exactly once, so results are deterministic. dtype FA_BF16, FA_F16 or FA_F32.
+ * Precision (FA_F32): every product runs on the fp32 matrix cores in fp32, P and dS
+ * included; the result matches the definition to fp32 rounding.
+ * Precision (FA_BF16, FA_F16): the matrix-core products run on fp16 operands with fp32
+ * accumulation.
  * dout is multiplied by a power of two (per query row in the dq kernel, per workgroup
  * from the 32-row maxima in the dk/dv kernel) that brings its largest magnitude into
  * [1, 2) before rounding, and the gradients are divided by it exactly at the end, so

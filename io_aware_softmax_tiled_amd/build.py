@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_bwd_dkdv.hip", "fa_merge.hip", "fa_deferred.hip",
-           "fa_noalloc.hip", "fa_api.cpp"]
+           "fa_bwd_f32.hip", "fa_noalloc.hip", "fa_api.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: never emit packed fp32 VALU (v_pk_{add,mul,fma}_f32).

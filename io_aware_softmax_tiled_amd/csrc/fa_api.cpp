@@ -97,11 +97,7 @@ namespace fa {
 // the size, dtype and scale checks of the backward entry points, without any pointer
 int bwd_check_sizes(int B, int H, int N, int d, float scale, int dtype) {
   clear_error();
-  const int st = check_common(B, H, N, d, scale, dtype);
-  if (st != FA_OK) return st;
-  if (dtype == FA_F32)
-    return fail(FA_EUNSUPPORTED, "the backward pass takes bf16 or f16 inputs, not f32");
-  return FA_OK;
+  return check_common(B, H, N, d, scale, dtype);
 }
 }  // namespace fa
 
@@ -333,8 +329,6 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* o, const 
   clear_error();
   int st = check_common(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
-  if (dtype == FA_F32)
-    return fail(FA_EUNSUPPORTED, "the backward pass takes bf16 or f16 inputs, not f32");
   if ((size_t)B * H * N == 0) return FA_OK;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
     return fail(FA_EINVAL, "null tensor pointer");

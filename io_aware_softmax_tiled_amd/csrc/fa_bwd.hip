@@ -386,7 +386,7 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d) {
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages) {
-  if (a.dtype == kDtypeF32) return hipErrorNotSupported;  // rejected by the API layer
+  if (a.dtype == kDtypeF32) return launch_bwd_f32(a, stream, stages);
   const int BH = a.B * a.H;
   const int n_groups = (a.N + kDmaxRows - 1) / kDmaxRows;
   const float sl2 = a.scale * kLog2e;

@@ -100,6 +100,8 @@ constexpr int kBwdAll = 2 | 4 | 8;
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages = kBwdAll);
 // the dK/dV kernel alone (fa_bwd_dkdv.hip; reads the D that bwd_pre wrote)
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+// fp32 inputs (fa_bwd_f32.hip): the same stages on the fp32 matrix cores
+hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t stream, int stages);
 
 // records msg as the thread's last error (fa_last_error) and returns status
 int api_fail(int status, const char* msg);

@@ -123,6 +123,10 @@ static void abi_backward() {
   CHECK(fa_bwd_sparse(P(0), P(1), P(2), (const float*)P(3), P(4), (const float*)P(5), (float*)P(6), (float*)P(7), (float*)P(8), B, H, N, d, 0.1f, 1, FA_BF16, nullptr, nullptr, P(9), ws, nullptr) == FA_EINVAL);
   CHECK(fa_bwd_dropout(P(0), P(1), P(2), (const float*)P(3), P(4), (const float*)P(5), (float*)P(6), (float*)P(7), (float*)P(8), B, H, N, d, 0.1f, 1, FA_BF16, nullptr, 0.5f, 9, 1, P(9), ws, nullptr) == FA_OK);
   CHECK(g_last_bwd.drop_t == 128);
+  // fp32 inputs have a backward pass (its own kernels behind the same launcher); the
+  // extensions do not
+  CHECK(call(P(9), ws, FA_F32, (float*)P(6)) == FA_OK && g_last_bwd.dtype == FA_F32);
+  CHECK(fa_bwd_dropout(P(0), P(1), P(2), (const float*)P(3), P(4), (const float*)P(5), (float*)P(6), (float*)P(7), (float*)P(8), B, H, N, d, 0.1f, 1, FA_F32, nullptr, 0.5f, 9, 1, P(9), ws, nullptr) == FA_EUNSUPPORTED);
   // status strings and the error buffer, including a message longer than the buffer
   for (int s = -1; s <= 5; ++s) CHECK(fa_status_str(s) != nullptr);
   CHECK(fa_version() > 0);

@@ -115,7 +115,7 @@ def test_workspace_size(lib):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=0), FA_EUNSUPPORTED),      # no fp32 backward
+    (dict(dtype=0, d=80), FA_EUNSUPPORTED),  # fp32 backward exists, head_dim 80 does not
     (dict(d=80), FA_EUNSUPPORTED),
     (dict(dq=None), FA_EINVAL),
     (dict(ws=None), FA_EWORKSPACE),
@@ -252,7 +252,8 @@ def test_bwd_stage_rejects_before_launch(lib):
     for bad in (-1, 4, 7):
         assert lib.fa_bwd_stage(bad, *args, P + 0x900000, ws, None) == FA_EINVAL
     assert lib.fa_bwd_stage(1, *args, None, 0, None) == FA_EWORKSPACE
-    args[15] = 0  # f32
+    args[15] = 0   # f32 (has a backward pass) with head_dim 80 (has none)
+    args[12] = 80
     assert lib.fa_bwd_stage(0, *args, P + 0x900000, ws, None) == FA_EUNSUPPORTED
 
 

@@ -43,7 +43,7 @@ def test_bwd_workload(cfg):
     U.say(f"  errors {rep}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 7, 65, 129, 257])
 @pytest.mark.parametrize("causal,pad", [(False, False), (True, False), (False, True),
@@ -185,3 +185,45 @@ def test_bwd_gradient_magnitude(dtype, mult):
     for name, t, i in (("dQ", dq, 0), ("dK", dk, 1), ("dV", dv, 2)):
         U.compare(name, _sel(t, heads).double() / mult, _stack(ref, heads, i) / mult, dtype, rep)
     U.say(f"  errors (relative to the gradient scale) {rep}")
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,kv,q_mult", [
+    (1, 1, 256, 64, False, None, 1.0),        # the fp32 workload's shape, with a backward pass
+    (2, 2, 1000, 128, True, None, 1.0),       # causal, several tiles
+    (2, 3, 517, 64, False, (100, 517), 1.0),  # key padding, ragged
+    (2, 2, 1000, 128, True, None, 4.0),       # peaky rows (scores of order 20)
+])
+def test_bwd_f32(B, H, N, d, causal, kv, q_mult):
+    """fp32 backward (fp32 matrix cores throughout) against the oracle at 1e-5 max-abs.
+    With peaky rows the scores reach |s| ~ 20 and fp32 rounding of s alone perturbs P by
+    ~2^-24 * |s| / scale relative, so the bar there is 1e-5 times the gradient's
+    magnitude (max(1, max|ref|)), the same relative accuracy."""
+    w, inp = workloads.custom(B, H, N, d, "f32", causal, kv_range=kv, q_mult=q_mult, seed=N)
+    U.say(f"[bwd] f32 B={B} H={H} N={N} d={d} causal={causal} kv={kv} q x{q_mult}")
+    o, lse, dq, dk, dv = U.gpu_bwd(inp)
+    ref = U.oracle_bwd(inp)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    rep = {}
+    for name, t, i in (("dQ", dq, 0), ("dK", dk, 1), ("dV", dv, 2)):
+        r = _stack(ref, heads, i)
+        mag = max(1.0, float(np.abs(r).max())) if q_mult != 1.0 else 1.0
+        U.compare(name, _sel(t, heads).double() / mag, r / mag, "f32", rep)
+    U.say(f"  errors {rep}")
+
+
+def test_bwd_f32_stages_match_fa_bwd():
+    """fp32: stages 0, 1, 2 give fa_bwd's results bit for bit."""
+    import io_aware_softmax_tiled_amd as fa
+    w, inp = workloads.custom(1, 2, 300, 128, "f32", True, seed=4)
+    dev = U.to_dev(inp)
+    o, lse = fa.fa_fwd(dev["q"], dev["k"], dev["v"], causal=True, scale=inp["scale"])
+    ref = fa.fa_bwd(dev["q"], dev["k"], dev["v"], o, dev["dout"], lse, causal=True,
+                    scale=inp["scale"])
+    outs = [torch.empty_like(ref[0]) for _ in range(3)]
+    ws = torch.empty(fa.fa_bwd_workspace_size(1, 2, 300, 128), dtype=torch.uint8, device="cuda")
+    for stage in (0, 1, 2):
+        fa.fa_bwd_stage(stage, dev["q"], dev["k"], dev["v"], o, dev["dout"], lse, *outs, ws,
+                        causal=True, scale=inp["scale"])
+    torch.cuda.synchronize()
+    for a, b in zip(outs, ref):
+        assert torch.equal(a, b)
