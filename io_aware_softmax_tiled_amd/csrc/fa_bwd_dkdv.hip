@@ -115,20 +115,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     __syncthreads();
     nt = tlist_len;
   }
-  // dO is taken times a power of two sc that brings the largest |dO| of the query rows
-  // this workgroup visits (from the 32-row maxima the D pass wrote) into [1, 2) before it
-  // is rounded to fp16; dP, D, dS and both accumulators scale with it, and the epilogue
-  // divides by sc (exact). Every wave forms the same value.
-  float sc;
-  {
-    const int ng = (N + kDmaxRows - 1) / kDmaxRows;
-    const float* mp = dmax + (size_t)bh * ng;
-    float m = 0.f;
-    for (int gi2 = i0 * (kBQ / kDmaxRows) + lane; gi2 < ng; gi2 += 64) m = fmaxf(m, mp[gi2]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    sc = pow2_scale(m);
-  }
   auto tile_at = [&](int s) {
     if constexpr (kSparse) return __builtin_amdgcn_readfirstlane((int)tlist[s]);
     else return i0 + s;
@@ -163,13 +149,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       s_dlt = delta[r];
     }
   };
+  // the power-of-two scale of dO (set below, before the first tile is stored)
+  float sc = 1.0f;
+  bool unscaled = true;
   auto store_tile = [&](FA_LDS uint8_t* qb, FA_LDS uint8_t* ob, FA_LDS float* st) {
 #pragma unroll
     for (int j = 0; j < kSC; ++j) {
       const int ci = tid + kThreads * j;
       const int row = ci / kCPR, ch = ci % kCPR;
       lds_write16(qb + tile_off<D>(row, ch), to_f16x8<T>(qs[j]));
-      lds_write16(ob + tile_off<D>(row, ch), to_f16x8_scaled<T>(os[j], sc));
+    }
+    if (unscaled) {  // wave-uniform: dO as it is
+#pragma unroll
+      for (int j = 0; j < kSC; ++j) {
+        const int ci = tid + kThreads * j;
+        lds_write16(ob + tile_off<D>(ci / kCPR, ci % kCPR), to_f16x8<T>(os[j]));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSC; ++j) {
+        const int ci = tid + kThreads * j;
+        lds_write16(ob + tile_off<D>(ci / kCPR, ci % kCPR), to_f16x8_scaled<T>(os[j], sc));
+      }
     }
     if (tid < kBQ) {
       st[tid] = s_lse;
@@ -213,6 +214,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       toff[r][db] = tile_off<D>(8 * hh + (gi >> 2) + 4 * r, db * 4 + 2 * (g & 1) + ((gi & 3) >> 1)) +
                     8 * (gi & 1);
 
+  // dO is taken times the power of two sc = pow2_scale(largest |dO| of the query rows this
+  // workgroup visits, from the 32-row maxima the D pass wrote) before it is rounded to
+  // fp16; dP, D, dS and both accumulators scale with it, and the epilogue divides by sc
+  // (exact). The maxima are read once the first tile's loads are in flight, so the two
+  // latencies overlap; every wave forms the same value.
+  {
+    const int ng = (N + kDmaxRows - 1) / kDmaxRows;
+    const float* mp = dmax + (size_t)bh * ng;
+    float m = 0.f;
+    for (int gi2 = i0 * (kBQ / kDmaxRows) + lane; gi2 < ng; gi2 += 64) m = fmaxf(m, mp[gi2]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    sc = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, pow2_scale(m))));
+  }
+  unscaled = sc == 1.0f;
   if (nt > 0) store_tile((FA_LDS uint8_t*)Qb0, (FA_LDS uint8_t*)Ob0, (FA_LDS float*)St0);
 
   // S = Q K^T and dP = dO V^T for the 32 queries of half `hf`:

@@ -122,13 +122,16 @@ template <typename T> __device__ inline float absmax8(u32x4 x) {
   return lo;
 }
 
-// Power-of-two scale that brings a magnitude m into [1, 2): 2^(1 - e) for m = f 2^e,
-// f in [0.5, 1), the exponent clamped so the scale stays a normal fp32; 1 for m = 0 or a
-// non-finite m. The backward pass multiplies dO by it before rounding to fp16, so dO,
-// dP and dS keep fp16's 11-bit precision whatever the magnitude of the gradient (the
-// scale is undone exactly in the fp32 epilogue).
+// Power-of-two scale for a largest magnitude m of dO: 1 while m lies in [2^-3, 2^4)
+// (there fp16 already holds dO, dP and dS with its full 11-bit precision and no risk of
+// overflow, since |dS| <= 2 max|dO|_2 max|V|_2), otherwise 2^(1 - e) for m = f 2^e,
+// f in [0.5, 1), which brings m into [1, 2) (the exponent clamped so the scale stays a
+// normal fp32); 1 for m = 0 or a non-finite m. The backward pass multiplies dO by it
+// before rounding to fp16 and divides the gradients by it exactly in the fp32 epilogue,
+// so small gradients do not sink into fp16 subnormals and large ones do not overflow.
 __device__ inline float pow2_scale(float m) {
   if (!(m > 0.f) || !(m <= 3.4e38f)) return 1.0f;
+  if (m >= 0.125f && m < 16.0f) return 1.0f;
   int e;
   (void)__builtin_frexpf(m, &e);
   const int x = min(126, max(-126, 1 - e));
