@@ -233,10 +233,22 @@ def main():
                          "TFLOP/s, % of peak and % of the roofline-attainable rate "
                          "(supplementary)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-workload", type=int, default=0, metavar="K",
+                    help="only run parity workload K's passes (fa_fwd, then fa_bwd when the "
+                         "workload has one), 10 untimed then 20 calls each: the program a "
+                         "profiler wraps to take per-kernel counters on that workload")
+    ap.add_argument("--summarize-profile", default="", metavar="DIR",
+                    help="no GPU work: read the rocprofv3 kernel-trace and counter passes "
+                         "under DIR (subfolders trace, fetch, write, sq, lds) and print a "
+                         "JSON summary per kernel (time, HBM bytes scaled by the copy "
+                         "calibration, MFMA busy, clock, LDS bank conflicts)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy a MIB-MiB buffer once (a plain copy kernel of known size, "
                          "to calibrate HBM byte counters in a profiler run)")
     args = ap.parse_args()
+    if args.summarize_profile:
+        print(json.dumps(summarize_profile(args.summarize_profile), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path (attention heads "
               "would shard across GPUs with no exchange between them).", file=sys.stderr)
@@ -259,6 +271,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.profile_workload:
+        profile_workload(fa, torch, workloads, args.profile_workload)
+        return
     w = workloads.WORKLOADS[WORKLOAD_ID]
     inp = workloads.draw(w)
     ms_step, fwd_ms, bwd_ms, per_kernel, stats, dev, ws = bench_workload(
@@ -518,6 +533,109 @@ def deferred(fa, torch, workloads):
             "single_pass_tflops": round(w.fwd_flops() / t_one / 1e9, 2),
             "deferred_tflops": round(w.fwd_flops() / t_def / 1e9, 2)}), flush=True)
 
+
+
+def profile_workload(fa, torch, workloads, wid, calls=20):
+    """Parity workload wid's passes, a fixed number of calls each, for a profiler run."""
+    w = workloads.WORKLOADS[wid]
+    inp = workloads.draw(w)
+    dev = {n: (None if inp[n] is None else inp[n].cuda()) for n in ("q", "k", "v", "dout")}
+    kvl = None if inp["kv_len"] is None else inp["kv_len"].cuda()
+    kw = dict(causal=w.causal, scale=w.scale, kv_len=kvl)
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8,
+                     device="cuda")
+    fns = [lambda: fa.fa_fwd(dev["q"], dev["k"], dev["v"], out=o, lse=lse, **kw)]
+    if w.has_bwd:
+        fns.append(lambda: fa.fa_bwd(dev["q"], dev["k"], dev["v"], o, dev["dout"], lse,
+                                     workspace=ws, **kw))
+    for fn in fns:
+        for _ in range(10 + calls):
+            fn()
+    torch.cuda.synchronize()
+    print(json.dumps({"profiled_workload": wid, "name": w.name, "calls_per_pass": 10 + calls}),
+          flush=True)
+
+
+def _kernel_name(name):
+    """Kernel template name without the namespace and the argument list."""
+    import re
+    n = re.sub(r"^void ", "", name).replace("fa::(anonymous namespace)::", "").replace("fa::", "")
+    depth, out = 0, ""
+    for ch in n:
+        if ch == "(" and depth == 0:
+            break
+        depth += (ch == "<") - (ch == ">")
+        out += ch
+    return out.strip()
+
+
+def summarize_profile(root, copy_mib=512):
+    """Per-kernel summary of rocprofv3 outputs under root: kernel trace stats (trace/),
+    FETCH_SIZE (fetch/), WRITE_SIZE, TCC_HIT, TCC_MISS (write/), SQ and GRBM counters
+    (sq/), LDS counters (lds/). HBM bytes are the counters scaled so that a plain device
+    copy of copy_mib MiB (launched first by --copy-calibration) reads and writes exactly
+    its size."""
+    import csv
+    import glob
+
+    def read_pass(sub):
+        per = {}
+        for f in glob.glob(os.path.join(root, sub, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    k = _kernel_name(row["Kernel_Name"])
+                    did = row.get("Dispatch_Id") or row.get("Correlation_Id")
+                    d = per.setdefault(k, {}).setdefault(row["Counter_Name"], {})
+                    d[did] = d.get(did, 0.0) + float(row["Counter_Value"])
+        return per
+
+    def mean(per):
+        return {k: {c: sum(v.values()) / len(v) for c, v in cs.items()} for k, cs in per.items()}
+
+    raw = {p: read_pass(p) for p in ("fetch", "write", "sq", "lds")}
+    passes = {p: mean(v) for p, v in raw.items()}
+
+    def copy(p):
+        # the calibration copy is the largest dispatch of any copy kernel in the pass (input
+        # staging may launch the same copy kernel on smaller buffers)
+        c = "FETCH_SIZE" if p == "fetch" else "WRITE_SIZE"
+        return {c: max(max(v[c].values()) for k, v in raw[p].items()
+                       if "copy" in k.lower() and c in v)}
+    nbytes = copy_mib << 20
+    fetch_factor = nbytes / (copy("fetch")["FETCH_SIZE"] * 1024)
+    write_factor = nbytes / (copy("write")["WRITE_SIZE"] * 1024)
+    trace = {}
+    for f in glob.glob(os.path.join(root, "trace", "**", "*kernel_stats.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                trace[_kernel_name(row["Name"])] = row
+    out = {"calibration": {"copy_mib": copy_mib, "fetch_factor": fetch_factor,
+                           "write_factor": write_factor}, "kernels": {}}
+    for k in passes["sq"]:
+        if not any(k.startswith(p) for p in ("fwd_", "bwd_", "merge_")):
+            continue
+        s, l = passes["sq"][k], passes["lds"].get(k, {})
+        fe, wr = passes["fetch"].get(k, {}), passes["write"].get(k, {})
+        gui = s["GRBM_GUI_ACTIVE"] / 8
+        e = {"calls": int(trace[k]["Calls"]) if k in trace else None,
+             "trace_avg_us": float(trace[k]["AverageNs"]) / 1e3 if k in trace else None,
+             "hbm_read_bytes": fe.get("FETCH_SIZE", 0.0) * 1024 * fetch_factor,
+             "hbm_write_bytes": wr.get("WRITE_SIZE", 0.0) * 1024 * write_factor,
+             "l2_hit_rate": (wr["TCC_HIT"] / max(wr["TCC_HIT"] + wr["TCC_MISS"], 1.0)
+                             if "TCC_HIT" in wr else None),
+             "mfma_busy_frac": s["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * 1024),
+             "mfma_insts": s["SQ_INSTS_MFMA"], "valu_insts": s["SQ_INSTS_VALU"],
+             "lds_insts": l.get("SQ_INSTS_LDS"),
+             "lds_bank_conflict_cycles": l.get("SQ_LDS_BANK_CONFLICT"),
+             "lds_active_cycles": l.get("SQ_LDS_IDX_ACTIVE"),
+             "gui_active_cycles_per_xcd": gui}
+        e["hbm_bytes_per_launch"] = e["hbm_read_bytes"] + e["hbm_write_bytes"]
+        if e["trace_avg_us"]:
+            e["clock_ghz"] = gui / (e["trace_avg_us"] * 1e3)
+        out["kernels"][k] = e
+    return out
 
 
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 matrix peak

@@ -223,7 +223,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
           if (qrow < N) {
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
             float* orow = Op + head + (size_t)qrow * D;
-    #pragma unroll
+#pragma unroll
             for (int c = 0; c < D / 8; ++c) *reinterpret_cast<f32x4*>(orow + 8 * c + 4 * hh) = z;
             if (hh == 0) LSEp[(size_t)pos.bh * N + qrow] = -INFINITY;
           }
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
       // that starts at the tile, so rows past the end of the sequence read as zeros.
       u32x4 ks[kVChunks], vs[kVChunks];
       uint32_t ld_off[kVChunks];   // byte offset of this thread's chunks inside a tile
-    #pragma unroll
+#pragma unroll
       for (int j = 0; j < kVChunks; ++j) {
         const int ci = tid + kThr * j;
         ld_off[j] = (uint32_t)((ci / kCPR) * D + (ci % kCPR) * 8) * 2;
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
         const uint32_t bytes = (uint32_t)max(N - n0, 0) * D * 2;
         const auto rk = buffer_rsrc(k + (size_t)n0 * D, bytes);
         const auto rv = buffer_rsrc(v + (size_t)n0 * D, bytes);
-    #pragma unroll
+#pragma unroll
         for (int j = 0; j < kVChunks; ++j) {
           kd[j] = buffer_load16(rk, ld_off[j]);
           vd[j] = buffer_load16(rv, ld_off[j]);
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
       auto load_kv = [&](int t) { load_kv_to(t, ks, vs); };
       auto store_kv_from = [&](FA_LDS uint8_t* kb, FA_LDS uint8_t* vb, const u32x4 (&kd)[kVChunks],
                                const u32x4 (&vd)[kVChunks]) {
-    #pragma unroll
+#pragma unroll
         for (int j = 0; j < kVChunks; ++j) {
           const int ci = tid + kThr * j;
           const int row = ci / kCPR, ch = ci % kCPR;
@@ -281,14 +281,14 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
 
       // Q fragment: B operand of S^T = K Q^T, lane (qi, hh) holds Q[qrow][16c + 8hh + 0..7]
       u32x4 qf[kKC];
-    #pragma unroll
+#pragma unroll
       for (int c = 0; c < kKC; ++c)
         qf[c] = *reinterpret_cast<const u32x4*>(q + (size_t)qrow_c * D + 16 * c + 8 * hh);
 
       f32x16 oacc[kDB];
-    #pragma unroll
+#pragma unroll
       for (int i = 0; i < kDB; ++i)
-    #pragma unroll
+#pragma unroll
         for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
 
       float m_ref = -INFINITY;  // reference maximum used in the exponent (raw score units)
@@ -300,12 +300,12 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
       // depends only on the low 4 bits of the row, so moving by 16 or 32 rows (and between
       // buffers) is a compile-time constant the LDS instructions take as an immediate offset.
       int koff[kKC];
-    #pragma unroll
+#pragma unroll
       for (int c = 0; c < kKC; ++c) koff[c] = tile_off<D>(krow_base, 2 * c + hh);
       int voff[2][kDB];
-    #pragma unroll
+#pragma unroll
       for (int r = 0; r < 2; ++r)
-    #pragma unroll
+#pragma unroll
         for (int db = 0; db < kDB; ++db)
           voff[r][db] = tile_off<D>(8 * hh + (gi >> 2) + 4 * r, db * 4 + 2 * (g & 1) + ((gi & 3) >> 1)) +
                         8 * (gi & 1);
@@ -326,13 +326,13 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
       u32x4 kf[kKC];          // K fragments (A operand) of the next score product
       u32x2 vf[2][kDB][2];    // V^T fragments (A operand) of the next P V product
       auto read_k = [&](const FA_LDS uint8_t* Ks, int sub) {
-    #pragma unroll
+#pragma unroll
         for (int c = 0; c < kKC; ++c) kf[c] = lds_read16(Ks + koff[c] + sub * 32 * D * 2);
       };
       auto read_v = [&](const FA_LDS uint8_t* Vs, int sub) {
-    #pragma unroll
+#pragma unroll
         for (int c2 = 0; c2 < 2; ++c2)
-    #pragma unroll
+#pragma unroll
           for (int db = 0; db < kDB; ++db) {
             const int rows = (32 * sub + 16 * c2) * D * 2;
             vf[c2][db][0] = lds_read_tr16(Vs + voff[0][db] + rows);
@@ -342,9 +342,9 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
       // S^T for 32 keys from the K fragments in kf
       auto scores = [&]() {
         f32x16 acc;
-    #pragma unroll
+#pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    #pragma unroll
+#pragma unroll
         for (int c = 0; c < kKC; ++c) acc = Mfma<T>::run(kf[c], qf[c], acc);
         return acc;
       };
@@ -358,14 +358,14 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
         if constexpr (kDropout) {
           const Philox4x32 ph = philox4x32((uint32_t)qrow, (uint32_t)(2 * sb + hh),
                                            (uint32_t)pos.bh, offset, seed_lo, seed_hi);
-    #pragma unroll
+#pragma unroll
           for (int w = 0; w < 4; ++w) rnd[w] = ph.w[w];
         }
         // (a row that has seen no visible key yet -- possible in a split or a sparse
         // pattern -- keeps
         // m_ref = -inf; its scores are all -inf and must give P = 0, not NaN)
         const float nms = (kGuard && m_ref == -INFINITY) ? 0.f : -m_ref * sl2;
-    #pragma unroll
+#pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float p0 = exp2_fast(fmaf(s[2 * i], sl2, nms));
           const float p1 = exp2_fast(fmaf(s[2 * i + 1], sl2, nms));
@@ -382,10 +382,10 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
       };
       // two 16-key steps of O^T += V^T P^T from the V^T fragments in vf
       auto pv = [&](const uint32_t (&pk)[8]) {
-    #pragma unroll
+#pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
           const u32x4 bp = {pk[4 * c2], pk[4 * c2 + 1], pk[4 * c2 + 2], pk[4 * c2 + 3]};
-    #pragma unroll
+#pragma unroll
           for (int db = 0; db < kDB; ++db)
             oacc[db] = Mfma<F16>::run(u32x4{vf[c2][db][0][0], vf[c2][db][0][1],
                                             vf[c2][db][1][0], vf[c2][db][1][1]},
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
       };
       auto rowmax = [&](const f32x16& s) {
         float mx = -INFINITY;
-    #pragma unroll
+#pragma unroll
         for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[r], s[r + 1]);
         return max_halves(mx);  // both halves of the wave hold the same query rows
       };
@@ -408,9 +408,9 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
           const float alpha = exp2_fast((m_ref - m_new) * sl2);  // 1 if kept, 0 from -inf
           m_ref = m_new;
           lsum *= alpha;
-    #pragma unroll
+#pragma unroll
           for (int i = 0; i < kDB; ++i)
-    #pragma unroll
+#pragma unroll
             for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
         }
       };
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
         }
         if (off || (n0 + 32 > kv_hi) || (causal && n0 + 31 > wq0)) {
           const int lim = off ? -1 : last_vis - n0;
-    #pragma unroll
+#pragma unroll
           for (int r = 0; r < 16; ++r) s[r] = (16 * (r >> 3) + (r & 7) > lim) ? -INFINITY : s[r];
         }
       };
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
       // keeps P in the region that computes it (the compiler would otherwise sink it into
       // the P V region, past the masking branch, and lose the overlap)
       auto pin = [&](const uint32_t (&pk)[8]) {
-    #pragma unroll
+#pragma unroll
         for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[i]));
       };
       // region A: each score MFMA followed by its share of the vector instructions (the 48
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
       // fragment reads
       auto hint_a = [&](auto nvalu) {
         constexpr int kPer = decltype(nvalu)::value / kKC;
-    #pragma unroll
+#pragma unroll
         for (int c = 0; c < kKC; ++c) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x402, kPer, 0);
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
       // region B: each P V MFMA followed by a K fragment read and a vector instruction of
       // the row maximum
       auto hint_b = [&]() {
-    #pragma unroll
+#pragma unroll
         for (int c = 0; c < 2 * kDB; ++c) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, (kKC + 2 * kDB - 1) / (2 * kDB), 0);
@@ -595,9 +595,9 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
         const bool empty = kGuard && !(ltot > 0.f);
         const float inv = empty ? 0.f : (kDropout ? keep_scale : 1.0f) / ltot;
         float* orow = Op + head + (size_t)qrow * D;
-    #pragma unroll
+#pragma unroll
         for (int db = 0; db < kDB; ++db)
-    #pragma unroll
+#pragma unroll
           for (int a4 = 0; a4 < 4; ++a4) {
             const f32x4 val = {oacc[db][4 * a4 + 0] * inv, oacc[db][4 * a4 + 1] * inv,
                                oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv};
