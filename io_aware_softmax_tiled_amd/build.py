@@ -15,8 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_bwd_dkdv.hip", "fa_merge.hip", "fa_deferred.hip",
-           "fa_bwd_f32.hip", "fa_noalloc.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_bwd_dkdv.hip", "fa_bwd_dkdv_pair.hip", "fa_merge.hip",
+           "fa_deferred.hip", "fa_bwd_f32.hip", "fa_noalloc.hip", "fa_api.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: never emit packed fp32 VALU (v_pk_{add,mul,fma}_f32).
@@ -26,10 +26,11 @@ HIPCC_FLAGS = [
     "-munsafe-fp-atomics", "-Wall", "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-# Per-source additions. The dK/dV kernel (one wave per SIMD, 392 registers) runs about
-# 6% faster with LLVM's iterative ILP scheduler than with the default, measured at
-# B=2 H=16 N=4096 d=128 and B=8 H=16 N=512 d=64; the other kernels are as fast or
-# faster with the default, so the option is confined to that file.
+# Per-source additions. The one-wave-per-SIMD dK/dV kernel (about 490 registers) runs
+# about 6% faster with LLVM's iterative ILP scheduler than with the default, measured at
+# B=2 H=16 N=4096 d=128 and B=8 H=16 N=512 d=64; the other kernels, the two-wave dK/dV
+# kernel of fa_bwd_dkdv_pair.hip included (5% slower under it), are as fast or faster
+# with the default, so the option is confined to that file.
 EXTRA_FLAGS = {
     "fa_bwd_dkdv.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }

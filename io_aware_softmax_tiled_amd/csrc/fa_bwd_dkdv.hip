@@ -8,6 +8,8 @@
 // tiles are prefetched one tile ahead through buffer resources and double-buffered:
 // one barrier per tile, waiting for LDS traffic only. Every matrix-core product runs in
 // fp16 with fp32 accumulation (Q, dO, K, V converted when staged; P and dS rounded).
+// At head_dim 128 without block mask or dropout the two-wave kernel of
+// fa_bwd_dkdv_pair.hip runs instead.
 //
 // This file is compiled on its own so that it can take its own instruction-scheduling
 // strategy (see the build script).
@@ -454,6 +456,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   do {                                                                        \
     if (a.block_mask != nullptr) FA_DKDV_LAUNCH2(TAG, DIM, true, false);      \
     else if (dropout) FA_DKDV_LAUNCH2(TAG, DIM, false, true);                 \
+    else if (DIM == 128) return launch_bwd_dkdv_pair(a, stream);              \
     else FA_DKDV_LAUNCH2(TAG, DIM, false, false);                             \
   } while (0)
   if (a.dtype == kDtypeBF16) {
