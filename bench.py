@@ -48,7 +48,7 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` (a name prefix such as "bwd_dkdv_kernel") from the
+    """HBM bytes per launch of `kernel` (a name prefix such as "bwd_dq_kernel") from the
     committed rocprofv3 counter runs, scaled by the copy-kernel calibration, or None when
     absent or taken on other kernel sources."""
     try:
@@ -146,8 +146,9 @@ def run_step(fa, dev, w, ws, events=None):
 
 # kernels of one step, in launch order, and the MFMA FLOPs each performs as a multiple
 # of the nominal forward count (the forward: 2 products; dQ: S, dP, dQ; dK/dV: S, dP,
-# dV, dK)
-KERNELS = [("fwd_kernel_16", 1.0), ("bwd_dq_kernel", 1.5), ("bwd_dkdv_kernel", 2.0)]
+# dV, dK); at this workload (head_dim 128, no block mask or dropout) the dK/dV stage runs
+# the two-wave kernel
+KERNELS = [("fwd_kernel_16", 1.0), ("bwd_dq_kernel", 1.5), ("bwd_dkdv_pair_kernel", 2.0)]
 
 
 # The GPU reaches its sustained clock only after tens of milliseconds of continuous
@@ -604,14 +605,18 @@ def summarize_profile(root, copy_mib=512):
         return {c: max(max(v[c].values()) for k, v in raw[p].items()
                        if "copy" in k.lower() and c in v)}
     nbytes = copy_mib << 20
-    fetch_factor = nbytes / (copy("fetch")["FETCH_SIZE"] * 1024)
-    write_factor = nbytes / (copy("write")["WRITE_SIZE"] * 1024)
+    try:
+        fetch_factor = nbytes / (copy("fetch")["FETCH_SIZE"] * 1024)
+        write_factor = nbytes / (copy("write")["WRITE_SIZE"] * 1024)
+    except ValueError:  # no byte-counter passes (or no calibration copy in them)
+        fetch_factor = write_factor = None
     trace = {}
     for f in glob.glob(os.path.join(root, "trace", "**", "*kernel_stats.csv"), recursive=True):
         with open(f) as fh:
             for row in csv.DictReader(fh):
                 trace[_kernel_name(row["Name"])] = row
-    out = {"calibration": {"copy_mib": copy_mib, "fetch_factor": fetch_factor,
+    out = {"source_hash": kernel_source_hash(),
+           "calibration": {"copy_mib": copy_mib, "fetch_factor": fetch_factor,
                            "write_factor": write_factor}, "kernels": {}}
     for k in passes["sq"]:
         if not any(k.startswith(p) for p in ("fwd_", "bwd_", "merge_")):
@@ -621,8 +626,10 @@ def summarize_profile(root, copy_mib=512):
         gui = s["GRBM_GUI_ACTIVE"] / 8
         e = {"calls": int(trace[k]["Calls"]) if k in trace else None,
              "trace_avg_us": float(trace[k]["AverageNs"]) / 1e3 if k in trace else None,
-             "hbm_read_bytes": fe.get("FETCH_SIZE", 0.0) * 1024 * fetch_factor,
-             "hbm_write_bytes": wr.get("WRITE_SIZE", 0.0) * 1024 * write_factor,
+             "hbm_read_bytes": (fe["FETCH_SIZE"] * 1024 * fetch_factor
+                                if fetch_factor and "FETCH_SIZE" in fe else None),
+             "hbm_write_bytes": (wr["WRITE_SIZE"] * 1024 * write_factor
+                                 if write_factor and "WRITE_SIZE" in wr else None),
              "l2_hit_rate": (wr["TCC_HIT"] / max(wr["TCC_HIT"] + wr["TCC_MISS"], 1.0)
                              if "TCC_HIT" in wr else None),
              "mfma_busy_frac": s["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * 1024),
@@ -630,8 +637,17 @@ def summarize_profile(root, copy_mib=512):
              "lds_insts": l.get("SQ_INSTS_LDS"),
              "lds_bank_conflict_cycles": l.get("SQ_LDS_BANK_CONFLICT"),
              "lds_active_cycles": l.get("SQ_LDS_IDX_ACTIVE"),
+             # LDS busy per compute unit; wave time waiting on LDS and issuing vector ALU
+             # instructions (SQ cycle counters count quad-cycles, alike for both terms)
+             "lds_active_frac": (l["SQ_LDS_IDX_ACTIVE"] / (256 * gui)
+                                 if "SQ_LDS_IDX_ACTIVE" in l else None),
+             "lds_wait_frac": (l["SQ_WAIT_INST_LDS"] / s["SQ_WAVE_CYCLES"]
+                               if "SQ_WAIT_INST_LDS" in l else None),
+             "valu_active_frac": (l["SQ_ACTIVE_INST_VALU"] / s["SQ_WAVE_CYCLES"]
+                                  if "SQ_ACTIVE_INST_VALU" in l else None),
              "gui_active_cycles_per_xcd": gui}
-        e["hbm_bytes_per_launch"] = e["hbm_read_bytes"] + e["hbm_write_bytes"]
+        if e["hbm_read_bytes"] is not None and e["hbm_write_bytes"] is not None:
+            e["hbm_bytes_per_launch"] = e["hbm_read_bytes"] + e["hbm_write_bytes"]
         if e["trace_avg_us"]:
             e["clock_ghz"] = gui / (e["trace_avg_us"] * 1e3)
         out["kernels"][k] = e
