@@ -8,8 +8,9 @@
 // tiles are prefetched one tile ahead through buffer resources and double-buffered:
 // one barrier per tile, waiting for LDS traffic only. Every matrix-core product runs in
 // fp16 with fp32 accumulation (Q, dO, K, V converted when staged; P and dS rounded).
-// At head_dim 128 without block mask or dropout the two-wave kernel of
-// fa_bwd_dkdv_pair.hip runs instead.
+// This kernel serves head_dim 64 (about 232 registers, so two workgroups, and two waves
+// per SIMD, share a compute unit); head_dim 128 runs the two-wave kernel of
+// fa_bwd_dkdv_pair.hip.
 //
 // This file is compiled on its own so that it can take its own instruction-scheduling
 // strategy (see the build script).
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     }
   };
 
-  // One 64-query tile: publish it (barrier), prefetch the next one, then (head_dim 64)
+  // One 64-query tile: publish it (barrier), prefetch the next one, then
   // three regions that keep the matrix cores busy while the vector units form P and dS:
   //   products of half 0 | products of half 1 with P, dS of half 0 |
   //   dV, dK products of half 0 with P, dS of half 1 | dV, dK products of half 1.
@@ -367,35 +368,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     if (active) {
       f32x16 s0, dp0, s1, dp1;
       uint32_t pp0[8], ds0[8], pp1[8], ds1[8];
-      if constexpr (D == 64) {
-        // three overlapped regions (see above)
-        products(Qc, Oc, 0, s0, dp0);
-        if (need_mask) mask(s0, q0, 0);
-        products(Qc, Oc, 1, s1, dp1);
-        p_ds(Stc, 0, s0, dp0, pp0, ds0);
-        hint(std::integral_constant<int, 2 * kKC>{}, std::integral_constant<int, 2 * kKC + 4>{});
-        pin(pp0, ds0);
-        if (need_mask) mask(s1, q0, 1);
-        accumulate(Qc, Oc, 0, pp0, ds0);
-        p_ds(Stc, 1, s1, dp1, pp1, ds1);
-        hint(std::integral_constant<int, 4 * kDB>{}, std::integral_constant<int, 8 * kDB + 4>{});
-        pin(pp1, ds1);
-        accumulate(Qc, Oc, 1, pp1, ds1);
-      } else {
-        // head_dim 128: both halves' products first, then P/dS and the dV/dK products
-        // per half, scheduled by the compiler (the overlapped regions measured slower
-        // here: twice the vector work per matrix product and the accumulators in AGPRs)
-        products(Qc, Oc, 0, s0, dp0);
-        products(Qc, Oc, 1, s1, dp1);
-        if (need_mask) {
-          mask(s0, q0, 0);
-          mask(s1, q0, 1);
-        }
-        p_ds(Stc, 0, s0, dp0, pp0, ds0);
-        accumulate(Qc, Oc, 0, pp0, ds0);
-        p_ds(Stc, 1, s1, dp1, pp1, ds1);
-        accumulate(Qc, Oc, 1, pp1, ds1);
-      }
+      // three overlapped regions (see above)
+      products(Qc, Oc, 0, s0, dp0);
+      if (need_mask) mask(s0, q0, 0);
+      products(Qc, Oc, 1, s1, dp1);
+      p_ds(Stc, 0, s0, dp0, pp0, ds0);
+      hint(std::integral_constant<int, 2 * kKC>{}, std::integral_constant<int, 2 * kKC + 4>{});
+      pin(pp0, ds0);
+      if (need_mask) mask(s1, q0, 1);
+      accumulate(Qc, Oc, 0, pp0, ds0);
+      p_ds(Stc, 1, s1, dp1, pp1, ds1);
+      hint(std::integral_constant<int, 4 * kDB>{}, std::integral_constant<int, 8 * kDB + 4>{});
+      pin(pp1, ds1);
+      accumulate(Qc, Oc, 1, pp1, ds1);
     }
     store_tile(Qn, On, Stn);  // tile it+1 (clamped) into the free buffers
   };
@@ -456,14 +441,11 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   do {                                                                        \
     if (a.block_mask != nullptr) FA_DKDV_LAUNCH2(TAG, DIM, true, false);      \
     else if (dropout) FA_DKDV_LAUNCH2(TAG, DIM, false, true);                 \
-    else if (DIM == 128) return launch_bwd_dkdv_pair(a, stream);              \
     else FA_DKDV_LAUNCH2(TAG, DIM, false, false);                             \
   } while (0)
-  if (a.dtype == kDtypeBF16) {
-    if (a.d == 64) FA_DKDV_LAUNCH(BF16, 64); else FA_DKDV_LAUNCH(BF16, 128);
-  } else {
-    if (a.d == 64) FA_DKDV_LAUNCH(F16, 64); else FA_DKDV_LAUNCH(F16, 128);
-  }
+  if (a.d == 128) return launch_bwd_dkdv_pair(a, stream);  // the two-wave kernel
+  if (a.dtype == kDtypeBF16) FA_DKDV_LAUNCH(BF16, 64);
+  else FA_DKDV_LAUNCH(F16, 64);
 #undef FA_DKDV_LAUNCH2
 #undef FA_DKDV_LAUNCH
   return hipGetLastError();

@@ -1,6 +1,6 @@
-// dK and dV at head_dim 128 without block mask or dropout: the keys-outer kernel of the
-// backward pass (fa_bwd_dkdv.hip has the general one, and fa_bwd.hip the rest of the
-// backward pass and the method it follows) with two waves per SIMD.
+// dK and dV at head_dim 128: the keys-outer kernel of the backward pass with two waves
+// per SIMD, with or without a block mask or dropout (fa_bwd_dkdv.hip has the one for
+// head_dim 64, and fa_bwd.hip the rest of the backward pass and the method it follows).
 //
 // Kept in a file of its own because it runs faster under the compiler's default
 // instruction scheduler, where the one-wave-per-SIMD kernel wants another strategy
@@ -28,14 +28,22 @@ constexpr int kBQ = 64;   // queries per tile (two 32-query halves)
 // ---------------------------------------------------------------------------------
 constexpr int kPairThreads = 512;
 
-template <typename T>
+//
+// kSparse: bmask is the n_sb x n_sb byte matrix over 128-query x 128-key blocks (this
+// workgroup's 128 keys are one key block); query tiles in disabled blocks are skipped.
+// kDropout: the probabilities carry the forward pass's dropout mask Z, regenerated from
+// the same Philox4x32-10 blocks (element (i, 32 g + u) of head bh: byte
+// 8 (u / 16) + u % 8 of the block at counter (i, 2 g + (u / 8) % 2, bh, offset); kept
+// iff >= drop_t): dV = (P Z / keep)^T dO, dP = (Z / keep) (dO V^T), dS = P (dP - D).
+template <typename T, bool kSparse, bool kDropout>
 __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_pair_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ delta,
     const float* __restrict__ dmax, float* __restrict__ dK, float* __restrict__ dV, int BH,
     int H, int N, float scale, float sl2, int causal, const int* __restrict__ kv_len,
-    int n_kblk, int heads_per_xcd) {
+    int n_kblk, int heads_per_xcd, const uint8_t* __restrict__ bmask, int n_sb,
+    uint32_t seed_lo, uint32_t seed_hi, uint32_t offset, int drop_t, float keep_scale) {
   constexpr int D = 128;
   constexpr int kKC = D / 16;
   constexpr int kDB = D / 32;
@@ -53,6 +61,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_pair_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
   __shared__ __attribute__((aligned(16))) float St0[2 * kBQ];  // LSE*log2(e), then D
   __shared__ __attribute__((aligned(16))) float St1[2 * kBQ];
+  __shared__ uint16_t tlist[kSparse ? 2 * kSparseMaxBlocks : 1];  // enabled query tiles
+  __shared__ int tlist_len;
+  // dropout: each wave's random bytes of the current tile, [its 32 queries][its 32 keys]
+  __shared__ __attribute__((aligned(16))) uint8_t zbuf[kDropout ? 8 * 32 * 32 : 16];
 
   const WgPos pos = wg_position(heads_per_xcd, blockIdx.x, BH);
   const int kblk = pos.blk;
@@ -87,7 +99,30 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_pair_kernel(
 
   const int nq = (N + kBQ - 1) / kBQ;
   const int i0 = causal ? k0 / kBQ : 0;
-  const int nt = max(nq - i0, 0);
+  // the query tiles this workgroup visits: i0 .. nq-1, or (sparse) those of them in
+  // query blocks enabled for this key block, listed by wave 0
+  int nt = max(nq - i0, 0);
+  if constexpr (kSparse) {
+    if (wave == 0) {
+      int count = 0;
+      for (int base = i0; base < nq; base += 64) {
+        const int it = base + lane;
+        const bool on = it < nq && bmask[(size_t)(it * kBQ / kSparseBlock) * n_sb + kblk] != 0;
+        const uint64_t m = __ballot(on);
+        const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (on) tlist[count + before] = (uint16_t)it;
+        count += __popcll(m);
+      }
+      if (lane == 0) tlist_len = count;
+    }
+    __syncthreads();
+    nt = tlist_len;
+  }
+  auto tile_at = [&](int s) {
+    if constexpr (kSparse) return __builtin_amdgcn_readfirstlane((int)tlist[s]);
+    else return i0 + s;
+  };
 
   u32x4 qs[kSC], os[kSC];
   float s_lse = 0.f, s_dlt = 0.f;
@@ -141,7 +176,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_pair_kernel(
     }
   };
 
-  if (nt > 0) load_tile(i0);
+  if (nt > 0) load_tile(tile_at(0));
 
   // the K and V block -> LDS as fp16 (rows past the end of the sequence as zeros)
   {
@@ -220,6 +255,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_pair_kernel(
       s[r] = (uint32_t)(rel - lo) < span ? s[r] : -INFINITY;
     }
   };
+  FA_LDS uint8_t* zw = (FA_LDS uint8_t*)zbuf + (kDropout ? wave * 32 * 32 : 0);  // wave bytes
   auto p_ds = [&](const FA_LDS float* Stc, const f32x16& s, const f32x16& dp, uint32_t (&pp)[8],
                   uint32_t (&dsp)[8]) {
 #pragma unroll
@@ -236,8 +272,15 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_pair_kernel(
         const float lq = j < 4 ? l0[j] : l1[j - 4];
         const float dq = j < 4 ? d0[j] : d1[j - 4];
         const float pj = exp2_fast(fmaf(s[r], sl2, -lq));
-        p[j] = pj;
-        ds[j] = pj * (dp[r] - dq);
+        if constexpr (kDropout) {
+          // byte of (query 16 c + 8 hh + j of this wave's half, this lane's key)
+          const bool keep = (int)zw[(16 * c + 8 * hh + j) * 32 + li] >= drop_t;
+          p[j] = keep ? pj : 0.f;                      // dV takes P Z (1/keep at the end)
+          ds[j] = pj * ((keep ? dp[r] * keep_scale : 0.f) - dq);
+        } else {
+          p[j] = pj;
+          ds[j] = pj * (dp[r] - dq);
+        }
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -269,13 +312,23 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_pair_kernel(
                   const FA_LDS float* Stc, FA_LDS uint8_t* Qn, FA_LDS uint8_t* On,
                   FA_LDS float* Stn) {
     barrier_lds();  // tile s (and, at s = 0, K and V) visible; the other buffers are free
-    load_tile(i0 + min(s + 1, nt - 1));
-    const int q0 = (i0 + s) * kBQ;
+    load_tile(tile_at(min(s + 1, nt - 1)));  // unconditional: same loads on every path
+    const int q0 = tile_at(s) * kBQ;
     const int hq0 = q0 + 32 * hf;  // first query of this wave's half
     // a half entirely above this wave's keys' diagonal, or past the sequence end, or a
     // wave whose keys are all padded, is skipped
     const bool active = !wave_dead && hq0 < N && !(causal && kw0 > hq0 + 31);
     const bool need_mask = (causal && kw0 + 31 > hq0) || (hq0 + 32 > N) || (kw0 + 32 > kv_lim);
+    if (kDropout && active) {
+      // lane (l, c) draws the block of (query hq0 + l % 32, this wave's keys 32 g + u with
+      // (u / 8) % 2 = c) and writes its bytes 0-7 (keys 8 c + 0..7) and 8-15 (keys
+      // 16 + 8 c + 0..7) to the wave's strip in key order; lanes then read their own key
+      const int c = lane >> 5;
+      const Philox4x32 blk = philox4x32((uint32_t)(hq0 + li), (uint32_t)(2 * (kw0 >> 5) + c),
+                                        (uint32_t)bh, offset, seed_lo, seed_hi);
+      *reinterpret_cast<FA_LDS u32x2*>(zw + li * 32 + 8 * c) = u32x2{blk.w[0], blk.w[1]};
+      *reinterpret_cast<FA_LDS u32x2*>(zw + li * 32 + 16 + 8 * c) = u32x2{blk.w[2], blk.w[3]};
+    }
     if (active) {
       f32x16 s0, dp0;
       uint32_t pp0[8], ds0[8];
@@ -315,7 +368,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_pair_kernel(
   if (hf == 0 && key < N) {
     float* dkr = dK + head + (size_t)key * D;
     float* dvr = dV + head + (size_t)key * D;
-    const float ks = scale / sc, vs = 1.0f / sc;
+    const float ks = scale / sc, vs = (kDropout ? keep_scale : 1.0f) / sc;
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
@@ -342,15 +395,28 @@ hipError_t launch_bwd_dkdv_pair(const BwdArgs& a, hipStream_t stream) {
   const auto* k16 = static_cast<const uint16_t*>(a.k);
   const auto* v16 = static_cast<const uint16_t*>(a.v);
   const auto* dO16 = static_cast<const uint16_t*>(a.dout);
-#define FA_DKDV_PAIR(TAG)                                                                  \
-  hipLaunchKernelGGL((bwd_dkdv_pair_kernel<TAG>), dim3(BH * n_kblk), dim3(kPairThreads), 0,  \
-                     stream, q16, k16, v16, dO16, a.lse, a.delta, a.dmax, a.dk, a.dv, BH, a.H, \
-                     a.N, a.scale, sl2, a.causal, a.kv_len, n_kblk, heads_per_xcd(BH))
-  if (a.d != 128 || a.block_mask != nullptr || a.drop_t >= 0) return hipErrorNotSupported;
+  const int n_sb = (a.N + kSparseBlock - 1) / kSparseBlock;
+  const bool dropout = a.drop_t >= 0;
+  const float keep_scale = dropout ? 256.0f / (float)(256 - a.drop_t) : 1.0f;
+  const uint32_t seed_lo = (uint32_t)a.seed, seed_hi = (uint32_t)(a.seed >> 32);
+#define FA_DKDV_PAIR2(TAG, SP, DR)                                                          \
+  hipLaunchKernelGGL((bwd_dkdv_pair_kernel<TAG, SP, DR>), dim3(BH * n_kblk),                \
+                     dim3(kPairThreads), 0, stream, q16, k16, v16, dO16, a.lse, a.delta,     \
+                     a.dmax, a.dk, a.dv, BH, a.H, a.N, a.scale, sl2, a.causal, a.kv_len,     \
+                     n_kblk, heads_per_xcd(BH), a.block_mask, n_sb, seed_lo, seed_hi,        \
+                     a.offset, a.drop_t, keep_scale)
+#define FA_DKDV_PAIR(TAG)                                                  \
+  do {                                                                     \
+    if (a.block_mask != nullptr) FA_DKDV_PAIR2(TAG, true, false);          \
+    else if (dropout) FA_DKDV_PAIR2(TAG, false, true);                     \
+    else FA_DKDV_PAIR2(TAG, false, false);                                 \
+  } while (0)
+  if (a.d != 128) return hipErrorNotSupported;
   if (a.dtype == kDtypeBF16) FA_DKDV_PAIR(BF16);
   else if (a.dtype == kDtypeF16) FA_DKDV_PAIR(F16);
   else return hipErrorNotSupported;
 #undef FA_DKDV_PAIR
+#undef FA_DKDV_PAIR2
   return hipGetLastError();
 }
 

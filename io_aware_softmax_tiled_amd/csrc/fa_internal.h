@@ -100,8 +100,8 @@ constexpr int kBwdAll = 2 | 4 | 8;
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages = kBwdAll);
 // the dK/dV kernel alone (fa_bwd_dkdv.hip; reads the D that bwd_pre wrote)
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
-// head_dim 128, bf16/f16, no block mask or dropout: the dK/dV kernel with two waves per
-// SIMD (fa_bwd_dkdv_pair.hip); launch_bwd_dkdv dispatches those cases to it
+// head_dim 128, bf16/f16: the dK/dV kernel with two waves per SIMD
+// (fa_bwd_dkdv_pair.hip); launch_bwd_dkdv dispatches those cases to it
 hipError_t launch_bwd_dkdv_pair(const BwdArgs& a, hipStream_t stream);
 // fp32 inputs (fa_bwd_f32.hip): the same stages on the fp32 matrix cores
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t stream, int stages);
