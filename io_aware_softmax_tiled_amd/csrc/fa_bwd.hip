@@ -285,8 +285,7 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         st[r] = 0.f;
-        // dense: the product accumulates dP - D (D is per query, so per lane)
-        dpt[r] = (kSparse || kDropout) ? 0.f : -dlt;
+        dpt[r] = 0.f;
       }
       // issue priority high in the two matrix-core phases of the sub-block and low in
       // the vector phase between them, so that the SIMD's other wave, when it is in a
@@ -323,16 +322,13 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(
       for (int i = 0; i < 8; ++i) {
         const float p0 = exp2_fast(fmaf(st[2 * i], sl2, -lse2));
         const float p1 = exp2_fast(fmaf(st[2 * i + 1], sl2, -lse2));
-        float dd0 = dpt[2 * i], dd1 = dpt[2 * i + 1];  // dP - D (dense), else dP
+        float dp0 = dpt[2 * i], dp1 = dpt[2 * i + 1];
         if constexpr (kDropout) {
           const uint32_t wv = rnd[i >> 1] >> (16 * (i & 1));
-          dd0 = ((int)(wv & 0xff) >= drop_t ? dd0 * keep_scale : 0.f) - dlt;
-          dd1 = ((int)((wv >> 8) & 0xff) >= drop_t ? dd1 * keep_scale : 0.f) - dlt;
-        } else if constexpr (kSparse) {
-          dd0 -= dlt;
-          dd1 -= dlt;
+          dp0 = (int)(wv & 0xff) >= drop_t ? dp0 * keep_scale : 0.f;
+          dp1 = (int)((wv >> 8) & 0xff) >= drop_t ? dp1 * keep_scale : 0.f;
         }
-        dsk[i] = Mfma<F16>::pack(p0 * dd0, p1 * dd1);
+        dsk[i] = Mfma<F16>::pack(p0 * (dp0 - dlt), p1 * (dp1 - dlt));
       }
       __builtin_amdgcn_s_setprio(1);
       // dQ^T += K^T dS^T: two 16-key steps; K^T through the transposing read
