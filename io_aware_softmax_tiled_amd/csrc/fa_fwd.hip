@@ -51,8 +51,6 @@ namespace fa {
 
 namespace {
 
-constexpr int kBM = 128;   // query rows per workgroup (4 waves x 32)
-
 // Item of round k for persistent workgroup p of P (-1 when done). Items u are numbered
 // heaviest first; with xcd, the items of one XCD (u = 8 v + x) are dealt to that XCD's
 // workgroups (p = 8 j + x) in a snake: v = k Px + j on even rounds, k Px + Px - 1 - j on
@@ -68,7 +66,6 @@ __device__ inline int snake_item(int p, int P, int n_items, int k, bool xcd) {
   return u < n_items ? u : -1;
 }
 constexpr int kBN = 64;    // key rows per tile
-constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------------------------
 // 16-bit inputs (bf16 or f16)
@@ -613,21 +610,34 @@ __global__ __launch_bounds__(W * 64, 8 / W) void fwd_kernel_16(
 }
 
 // ---------------------------------------------------------------------------------
-// fp32 inputs: the same S^T / O^T orientation on the 32x32x2 fp32 matrix cores.
+// fp32 inputs: 32x32x2 fp32 matrix cores, one workgroup per 32 query rows of a head.
+// The key axis of the row group is split over the workgroup's KS waves: wave w takes the
+// 32-key sub-blocks w, w + KS, w + 2 KS, ... and keeps its own reference maximum, row sum
+// and unnormalised O^T; at the end the KS partial states are combined through LDS as
+// split-KV partials are, M = max_w m_w, L = sum_w e^{m_w - M} l_w,
+// O = sum_w e^{m_w - M} O_w / L, LSE = M + ln L (the same online-softmax identity the
+// per-tile update uses). The fp32 products take 64 cycles each, so a row group's chain of
+// products is the latency of a small problem; splitting its keys over KS SIMDs shortens
+// that chain KS-fold. Each wave reads its K and V fragments straight from global memory.
+// Head-dim order inside the score product: step c pairs element c of the lane half
+// hh = 0 with element D/2 + c of the half hh = 1, so each lane's Q and K fragments are
+// contiguous halves of their rows (any order of the head_dim sum gives S).
 // ---------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(kThreads, 1) void fwd_kernel_f32(
+template <int D, int KS>
+__global__ __launch_bounds__(KS * 64, 1) void fwd_kernel_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int BH, int H, int N, float scale,
-    float sl2, int causal, const int* __restrict__ kv_len, int n_mblk, int heads_per_xcd) {
-  constexpr int kLd = D + 4;                   // padded row (floats)
-  constexpr int kDB = D / 32;
-  __shared__ __attribute__((aligned(16))) float Ks[kBN * kLd];
-  __shared__ __attribute__((aligned(16))) float Vs[kBN * kLd];
+    float sl2, int causal, const int* __restrict__ kv_len, int n_rg, int heads_per_xcd) {
+  constexpr int kDB = D / 32;   // 32-row blocks of O^T
+  constexpr int kHalf = D / 2;  // head_dim elements per lane half
+  constexpr int kLd = 33;       // padded query stride of the partial O^T in LDS
+  __shared__ float so[KS][D * kLd];  // partial O^T of each wave, [d][query]
+  __shared__ float sm[KS][32];       // reference maximum of each wave, per query
+  __shared__ float sl[KS][32];       // row sum of each wave, per query
 
   const WgPos pos = wg_position(heads_per_xcd, blockIdx.x, BH);
   if (pos.bh >= BH) return;
-  const int mblk = n_mblk - 1 - pos.blk;  // heaviest query block first
+  const int rg = n_rg - 1 - pos.blk;  // heaviest row group first
   const int b = pos.bh / H;
   const size_t head = (size_t)pos.bh * N * D;
   const float* q = Q + head;
@@ -635,91 +645,83 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel_f32(
   const float* v = V + head;
   int kv_lim = N;
   if (kv_len != nullptr) kv_lim = min(N, max(1, kv_len[b]));
-  const int m0 = mblk * kBM;
-  const int kend = causal ? min(kv_lim, m0 + kBM) : kv_lim;
-  const int ntiles = (kend + kBN - 1) / kBN;
+  const int r0 = rg * 32;
+  // every sub-block below nsub holds a key that every row of the group can see (its first
+  // key is below kv_lim and, under the causal mask, not after the group's first row)
+  const int kend = causal ? min(kv_lim, r0 + 32) : kv_lim;
+  const int nsub = (kend + 31) / 32;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int qi = lane & 31;
   const int hh = lane >> 5;
-  const int wq0 = m0 + wave * 32;
-  const int qrow = wq0 + qi;
+  const int qrow = r0 + qi;
   const int qrow_c = min(qrow, N - 1);
 
-  // Q fragment: lane (qi, hh) holds Q[qrow][2c + hh], c = 0..D/2-1
-  float qf[D / 2];
+  // Q fragment (B operand): lane (qi, hh) holds Q[qrow][hh D/2 + c], c < D/2
+  float qf[kHalf];
 #pragma unroll
-  for (int c = 0; c < D / 2; ++c) qf[c] = q[(size_t)qrow_c * D + 2 * c + hh];
+  for (int c = 0; c < kHalf; c += 4) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(q + (size_t)qrow_c * D + hh * kHalf + c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qf[c + j] = x[j];
+  }
 
   f32x16 oacc[kDB];
 #pragma unroll
   for (int i = 0; i < kDB; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-  float m_ref = -INFINITY;
-  float lsum = 0.f;
-  const int krow_base = kappa(qi);
+  float m_ref = -INFINITY;  // raw score units
+  float lsum = 0.f;         // this lane's half of the row sum
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int n0 = t * kBN;
-    __syncthreads();
-    for (int e = threadIdx.x; e < kBN * D / 4; e += kThreads) {
-      const int row = e / (D / 4), c4 = e % (D / 4);
-      const size_t goff = (size_t)min(n0 + row, N - 1) * D + 4 * c4;
-      const f32x4 kv4 = *reinterpret_cast<const f32x4*>(k + goff);
-      const f32x4 vv4 = *reinterpret_cast<const f32x4*>(v + goff);
+  for (int j = wave; j < nsub; j += KS) {
+    const int n0 = 32 * j;
+    // K fragment (A operand of S^T = K Q^T): row n0 + qi, the lane's half of head_dim.
+    // Rows past the end of the sequence are clamped to the last row (finite values) and
+    // masked below.
+    float kf[kHalf];
+    const float* krow = k + (size_t)min(n0 + qi, N - 1) * D + hh * kHalf;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        Ks[row * kLd + 4 * c4 + j] = kv4[j];
-        Vs[row * kLd + 4 * c4 + j] = vv4[j];
-      }
+    for (int c = 0; c < kHalf; c += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(krow + c);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) kf[c + t] = x[t];
     }
-    __syncthreads();
-
-    bool vis[2];
+    // V fragments (A operand of O^T += V^T P^T): accumulator register r of lane (qi, hh)
+    // holds key n0 + 8 (r / 4) + 4 hh + r % 4, so the product's step r takes that key's V
+    // row, element 32 db + qi
+    float vf[kDB][16];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-      vis[sub] = (n0 + 32 * sub < kv_lim) && (!causal || n0 + 32 * sub <= wq0 + 31);
-    if (!vis[0] && !vis[1]) continue;
-
-    f32x16 sacc[2];
+    for (int r = 0; r < 16; ++r) {
+      const float* vrow = v + (size_t)min(n0 + 8 * (r >> 2) + 4 * hh + (r & 3), N - 1) * D + qi;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[sub][r] = 0.f;
-      if (vis[sub]) {
-        const float* krow = Ks + (sub * 32 + krow_base) * kLd;
-#pragma unroll
-        for (int c = 0; c < D / 2; ++c)
-          sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * c + hh], qf[c], sacc[sub],
-                                                           0, 0, 0);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[sub][r] = -INFINITY;
-      }
+      for (int db = 0; db < kDB; ++db) vf[db][r] = vrow[32 * db];
     }
-    const bool need_mask = (n0 + kBN > kv_lim) || (causal && n0 + kBN - 1 > wq0);
-    if (need_mask) {
+
+    f32x16 s;
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = n0 + 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
-          const bool hide = key >= kv_lim || (causal && key > qrow);
-          sacc[sub][r] = hide ? -INFINITY : sacc[sub][r];
-        }
+    for (int c = 0; c < kHalf; ++c) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[c], qf[c], s, 0, 0, 0);
+
+    if (n0 + 32 > kv_lim || (causal && n0 + 31 > r0)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = n0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const bool hide = key >= kv_lim || (causal && key > qrow);
+        s[r] = hide ? -INFINITY : s[r];
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = max3f(mx, sacc[sub][r], sacc[sub][r + 1]);
+    for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[r], s[r + 1]);
     mx = max_halves(mx);
+    // the reference maximum is raised only when the exponent would exceed 2^8
     const bool grow = (mx - m_ref) * sl2 > 8.0f;
     if (__any(grow)) {
       const float m_new = grow ? mx : m_ref;
-      const float alpha = exp2_fast((m_ref - m_new) * sl2);
+      const float alpha = exp2_fast((m_ref - m_new) * sl2);  // 1 if kept, 0 from -inf
       m_ref = m_new;
       lsum *= alpha;
 #pragma unroll
@@ -729,40 +731,64 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel_f32(
     }
     const float nms = -m_ref * sl2;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sacc[sub][r] = exp2_fast(fmaf(sacc[sub][r], sl2, nms));
-        lsum += sacc[sub][r];
-      }
-    // O^T += V^T P^T, one key per half-wave per instruction
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      if (!vis[sub]) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
-#pragma unroll
-        for (int db = 0; db < kDB; ++db)
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * kLd + db * 32 + qi],
-                                                          sacc[sub][r], oacc[db], 0, 0, 0);
-      }
+    for (int r = 0; r < 16; ++r) {
+      s[r] = exp2_fast(fmaf(s[r], sl2, nms));
+      lsum += s[r];
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf[db][r], s[r], oacc[db], 0, 0, 0);
   }
 
+  // partial states -> LDS (a wave that took no sub-block leaves m = -inf, l = 0, O = 0)
   const float ltot = sum_halves(lsum);
-  if (qrow < N) {
-    const float inv = 1.0f / ltot;
-    float* orow = O + head + (size_t)qrow * D;
+  if (hh == 0) {
+    sm[wave][qi] = m_ref;
+    sl[wave][qi] = ltot;
+  }
 #pragma unroll
-    for (int db = 0; db < kDB; ++db)
+  for (int db = 0; db < kDB; ++db)
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const f32x4 val = {oacc[db][4 * a4 + 0] * inv, oacc[db][4 * a4 + 1] * inv,
-                           oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv};
-        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * a4 + 4 * hh) = val;
+    for (int r = 0; r < 16; ++r)
+      so[wave][(32 * db + 8 * (r >> 2) + 4 * hh + (r & 3)) * kLd + qi] = oacc[db][r];
+  __syncthreads();
+
+  // combination: thread t owns query row t / TPR and EPT consecutive head_dim columns
+  constexpr int kTPR = KS * 64 / 32;
+  constexpr int kEPT = D / kTPR;
+  static_assert(kEPT % 4 == 0, "16-byte output stores");
+  const int row = threadIdx.x / kTPR;
+  const int d0 = (threadIdx.x % kTPR) * kEPT;
+  const int orow_i = r0 + row;
+  if (orow_i < N) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < KS; ++w) M = fmaxf(M, sm[w][row]);
+    float cw[KS];
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < KS; ++w) {
+      const float mw = sm[w][row];
+      cw[w] = mw == -INFINITY ? 0.f : exp2_fast((mw - M) * sl2);
+      L += cw[w] * sl[w][row];
+    }
+    const float inv = 1.0f / L;
+    float* orow = O + head + (size_t)orow_i * D;
+#pragma unroll
+    for (int e = 0; e < kEPT; e += 4) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < KS; ++w) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] += cw[w] * so[w][(d0 + e + t) * kLd + row];
       }
-    if (hh == 0) LSE[(size_t)pos.bh * N + qrow] = m_ref * scale + __logf(ltot);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t] *= inv;
+      *reinterpret_cast<f32x4*>(orow + d0 + e) = acc;
+    }
+    if (d0 == 0) LSE[(size_t)pos.bh * N + orow_i] = M * scale + log2_fast(L) * kLn2;
   }
 }
 
@@ -837,18 +863,21 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     else if (dropout) FA_LAUNCH16(TAG, DIM, 3);      \
     else FA_LAUNCH16(TAG, DIM, 0);                   \
   } while (0)
-#define FA_LAUNCH32(DIM)                                                                  \
-  hipLaunchKernelGGL((fwd_kernel_f32<DIM>), dim3(g.blocks), dim3(kThreads), 0, stream,    \
-                     static_cast<const float*>(a.q), static_cast<const float*>(a.k),       \
-                     static_cast<const float*>(a.v), a.o, a.lse, BH, a.H, a.N, a.scale, sl2, \
-                     a.causal, a.kv_len, g.n_mblk, g.heads_per_xcd)
+  // fp32: one workgroup per 32 query rows, the keys split over 8 waves at head_dim 64 and
+  // over 4 at 128 (its fragments need more than the 256 registers of two waves per SIMD)
+  const int n_rg = (a.N + 31) / 32;
+#define FA_LAUNCH32(DIM, KS)                                                                \
+  hipLaunchKernelGGL((fwd_kernel_f32<DIM, KS>), dim3(BH * n_rg), dim3(KS * 64), 0, stream,  \
+                     static_cast<const float*>(a.q), static_cast<const float*>(a.k),         \
+                     static_cast<const float*>(a.v), a.o, a.lse, BH, a.H, a.N, a.scale, sl2,   \
+                     a.causal, a.kv_len, n_rg, g.heads_per_xcd)
   if (a.dtype == kDtypeBF16) {
     if (a.d == 64) FA_LAUNCH16P(BF16, 64); else FA_LAUNCH16P(BF16, 128);
   } else if (a.dtype == kDtypeF16) {
     if (a.d == 64) FA_LAUNCH16P(F16, 64); else FA_LAUNCH16P(F16, 128);
   } else {
     if (partial || sparse || dropout) return hipErrorNotSupported;  // rejected by the API
-    if (a.d == 64) FA_LAUNCH32(64); else FA_LAUNCH32(128);
+    if (a.d == 64) FA_LAUNCH32(64, 8); else FA_LAUNCH32(128, 4);
   }
 #undef FA_LAUNCH16P
 #undef FA_LAUNCH16
