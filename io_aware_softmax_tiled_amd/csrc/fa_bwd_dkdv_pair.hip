@@ -1,6 +1,8 @@
-// dK and dV at head_dim 128: the keys-outer kernel of the backward pass with two waves
-// per SIMD, with or without a block mask or dropout (fa_bwd_dkdv.hip has the one for
-// head_dim 64, and fa_bwd.hip the rest of the backward pass and the method it follows).
+// dK and dV: the keys-outer kernel of the backward pass with two waves per SIMD, with or
+// without a block mask or dropout, for every head_dim-128 backward and for head_dim-64
+// ones whose grid is too small to give every compute unit two workgroups of the
+// one-wave kernel in fa_bwd_dkdv.hip (fa_bwd.hip has the rest of the backward pass and
+// the method it follows).
 //
 // Kept in a file of its own because it runs faster under the compiler's default
 // instruction scheduler, where the one-wave-per-SIMD kernel wants another strategy
@@ -35,7 +37,7 @@ constexpr int kPairThreads = 512;
 // the same Philox4x32-10 blocks (element (i, 32 g + u) of head bh: byte
 // 8 (u / 16) + u % 8 of the block at counter (i, 2 g + (u / 8) % 2, bh, offset); kept
 // iff >= drop_t): dV = (P Z / keep)^T dO, dP = (Z / keep) (dO V^T), dS = P (dP - D).
-template <typename T, bool kSparse, bool kDropout>
+template <typename T, int D, bool kSparse, bool kDropout>
 __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_pair_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -44,7 +46,6 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_pair_kernel(
     int H, int N, float scale, float sl2, int causal, const int* __restrict__ kv_len,
     int n_kblk, int heads_per_xcd, const uint8_t* __restrict__ bmask, int n_sb,
     uint32_t seed_lo, uint32_t seed_hi, uint32_t offset, int drop_t, float keep_scale) {
-  constexpr int D = 128;
   constexpr int kKC = D / 16;
   constexpr int kDB = D / 32;
   constexpr int kCPR = D / 8;                            // 16-byte chunks per row
@@ -53,11 +54,12 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_pair_kernel(
   constexpr int kSC = kTile / 16 / kPairThreads;         // staged chunks per thread per tensor
   constexpr int kKVC = kKV / 16 / kPairThreads;          // K/V chunks per thread
   // LDS: K, V blocks, then two Q and two dO tile buffers; after the loop the whole
-  // region holds the partial accumulators of waves 4-7 (4 x 32 KiB)
+  // region holds the partial accumulators of waves 4-7 (4 x 8 kDB KiB)
   constexpr int kOffV = kKV, kOffQ0 = 2 * kKV, kOffQ1 = kOffQ0 + kTile;
   constexpr int kOffO0 = kOffQ1 + kTile, kOffO1 = kOffO0 + kTile;
   constexpr int kLds = kOffO1 + kTile;
-  static_assert(kLds >= 4 * 64 * 2 * kDB * 16 * 4, "reduction area");
+  constexpr int kRed = 2 * kDB * 4;  // 16-byte chunks of partial dK and dV per lane
+  static_assert(kLds >= 4 * 64 * kRed * 16, "reduction area");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
   __shared__ __attribute__((aligned(16))) float St0[2 * kBQ];  // LSE*log2(e), then D
   __shared__ __attribute__((aligned(16))) float St1[2 * kBQ];
@@ -350,9 +352,9 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_pair_kernel(
   }
 
   // the pairs add their partial accumulators: waves 4-7 write theirs to LDS (chunk j of
-  // 4 floats of lane l at ((kg * 32 + j) * 64 + l) * 16), waves 0-3 add them and store
+  // 4 floats of lane l at ((kg * kRed + j) * 64 + l) * 16), waves 0-3 add them and store
   __syncthreads();
-  FA_LDS f32x4* red = (FA_LDS f32x4*)lds + kg * 32 * 64 + lane;
+  FA_LDS f32x4* red = (FA_LDS f32x4*)lds + kg * kRed * 64 + lane;
   if (hf == 1) {
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
@@ -360,7 +362,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_pair_kernel(
       for (int a4 = 0; a4 < 4; ++a4) {
         red[(db * 4 + a4) * 64] = f32x4{dkacc[db][4 * a4], dkacc[db][4 * a4 + 1],
                                         dkacc[db][4 * a4 + 2], dkacc[db][4 * a4 + 3]};
-        red[(16 + db * 4 + a4) * 64] = f32x4{dvacc[db][4 * a4], dvacc[db][4 * a4 + 1],
+        red[(4 * kDB + db * 4 + a4) * 64] = f32x4{dvacc[db][4 * a4], dvacc[db][4 * a4 + 1],
                                              dvacc[db][4 * a4 + 2], dvacc[db][4 * a4 + 3]};
       }
   }
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_pair_kernel(
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int d0 = 32 * db + 8 * a4 + 4 * hh;
-        const f32x4 pk = red[(db * 4 + a4) * 64], pv = red[(16 + db * 4 + a4) * 64];
+        const f32x4 pk = red[(db * 4 + a4) * 64], pv = red[(4 * kDB + db * 4 + a4) * 64];
         const f32x4 kk = {ks * (dkacc[db][4 * a4] + pk[0]), ks * (dkacc[db][4 * a4 + 1] + pk[1]),
                           ks * (dkacc[db][4 * a4 + 2] + pk[2]), ks * (dkacc[db][4 * a4 + 3] + pk[3])};
         const f32x4 vv = {vs * (dvacc[db][4 * a4] + pv[0]), vs * (dvacc[db][4 * a4 + 1] + pv[1]),
@@ -399,23 +401,29 @@ hipError_t launch_bwd_dkdv_pair(const BwdArgs& a, hipStream_t stream) {
   const bool dropout = a.drop_t >= 0;
   const float keep_scale = dropout ? 256.0f / (float)(256 - a.drop_t) : 1.0f;
   const uint32_t seed_lo = (uint32_t)a.seed, seed_hi = (uint32_t)(a.seed >> 32);
-#define FA_DKDV_PAIR2(TAG, SP, DR)                                                          \
-  hipLaunchKernelGGL((bwd_dkdv_pair_kernel<TAG, SP, DR>), dim3(BH * n_kblk),                \
+#define FA_DKDV_PAIR2(TAG, DIM, SP, DR)                                                     \
+  hipLaunchKernelGGL((bwd_dkdv_pair_kernel<TAG, DIM, SP, DR>), dim3(BH * n_kblk),           \
                      dim3(kPairThreads), 0, stream, q16, k16, v16, dO16, a.lse, a.delta,     \
                      a.dmax, a.dk, a.dv, BH, a.H, a.N, a.scale, sl2, a.causal, a.kv_len,     \
                      n_kblk, heads_per_xcd(BH), a.block_mask, n_sb, seed_lo, seed_hi,        \
                      a.offset, a.drop_t, keep_scale)
-#define FA_DKDV_PAIR(TAG)                                                  \
+#define FA_DKDV_PAIR1(TAG, DIM)                                            \
   do {                                                                     \
-    if (a.block_mask != nullptr) FA_DKDV_PAIR2(TAG, true, false);          \
-    else if (dropout) FA_DKDV_PAIR2(TAG, false, true);                     \
-    else FA_DKDV_PAIR2(TAG, false, false);                                 \
+    if (a.block_mask != nullptr) FA_DKDV_PAIR2(TAG, DIM, true, false);     \
+    else if (dropout) FA_DKDV_PAIR2(TAG, DIM, false, true);                \
+    else FA_DKDV_PAIR2(TAG, DIM, false, false);                            \
   } while (0)
-  if (a.d != 128) return hipErrorNotSupported;
+#define FA_DKDV_PAIR(TAG)                                \
+  do {                                                   \
+    if (a.d == 128) FA_DKDV_PAIR1(TAG, 128);             \
+    else FA_DKDV_PAIR1(TAG, 64);                         \
+  } while (0)
+  if (a.d != 128 && a.d != 64) return hipErrorNotSupported;
   if (a.dtype == kDtypeBF16) FA_DKDV_PAIR(BF16);
   else if (a.dtype == kDtypeF16) FA_DKDV_PAIR(F16);
   else return hipErrorNotSupported;
 #undef FA_DKDV_PAIR
+#undef FA_DKDV_PAIR1
 #undef FA_DKDV_PAIR2
   return hipGetLastError();
 }

@@ -810,9 +810,7 @@ FwdGrid fwd_grid(int B, int H, int N, int waves) {
   return g;
 }
 
-// Workgroups of a persistent grid: the items, capped at per_cu resident workgroups on
-// every compute unit (a multiple of 8, the XCD count).
-static int persistent_grid(int items, int per_cu) {
+int device_cu_count() {
   static int cus = 0;
   if (cus == 0) {
     int dev = 0, n = 0;
@@ -822,7 +820,13 @@ static int persistent_grid(int items, int per_cu) {
     else
       cus = 256;
   }
-  const int cap = cus * per_cu;
+  return cus;
+}
+
+// Workgroups of a persistent grid: the items, capped at per_cu resident workgroups on
+// every compute unit (a multiple of 8, the XCD count).
+static int persistent_grid(int items, int per_cu) {
+  const int cap = device_cu_count() * per_cu;
   return items < cap ? items : cap;
 }
 

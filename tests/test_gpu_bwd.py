@@ -59,6 +59,23 @@ def test_bwd_small(dtype, d, N, causal, pad):
         U.compare(name, _sel(t, heads), _stack(ref, heads, i), dtype)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,pad", [(False, False), (True, False), (False, True),
+                                       (True, True)])
+def test_bwd_wide_grid(d, causal, pad):
+    """B*H*ceil(N/128) = 768 dK/dV workgroups, three per compute unit: head_dim 64 runs
+    the one-wave dK/dV kernel here (smaller grids run the two-wave one); every head."""
+    N = 300
+    w, inp = workloads.custom(8, 32, N, d, "bf16", causal, kv_range=(1, N) if pad else None,
+                              seed=41 + d)
+    U.say(f"[bwd] wide grid N={N} d={d} causal={causal} pad={pad}")
+    o, lse, dq, dk, dv = U.gpu_bwd(inp)
+    heads = [(b, h) for b in range(8) for h in range(32)]
+    ref = U.oracle_bwd(inp, heads=heads)
+    for name, t, i in (("dQ", dq, 0), ("dK", dk, 1), ("dV", dv, 2)):
+        U.compare(name, _sel(t, heads), _stack(ref, heads, i), "bf16")
+
+
 @pytest.mark.parametrize("N", [447, 511, 575, 703])
 def test_causal_padded_mid_sizes(N):
     """Causal with key padding at head_dim 128 over two or three 256-row query blocks: the

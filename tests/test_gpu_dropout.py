@@ -56,6 +56,28 @@ def test_dropout_small(dtype, d, N, causal, pad):
     U.compare("dV", dv, rv, dtype)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_wide_grid(d, causal):
+    """B*H*ceil(N/128) = 768 dK/dV workgroups (head_dim 64: the one-wave dK/dV kernel)."""
+    N = 300
+    w, inp = workloads.custom(8, 32, N, d, "bf16", causal, kv_range=(1, N), seed=750 + d)
+    p, seed, offset = 0.17, 4321 + d, 9
+    U.say(f"[dropout] wide grid N={N} d={d} causal={causal} p={p} seed={seed}")
+    o, lse, (dq, dk, dv) = _run(inp, p, seed, offset)
+    q, k, v, do = (U.f64(inp, n) for n in ("q", "k", "v", "dout"))
+    kvn = U.kv_np(inp)
+    ref_o, ref_l = oracle.attention_forward_dropout(q, k, v, inp["scale"], causal, kvn, p,
+                                                    seed, offset)
+    U.compare("O", o, ref_o, "bf16")
+    U.compare("LSE", lse, ref_l, "bf16")
+    rq, rk, rv = oracle.attention_backward_dropout(q, k, v, do, inp["scale"], causal, kvn, p,
+                                                   seed, offset)
+    U.compare("dQ", dq, rq, "bf16")
+    U.compare("dK", dk, rk, "bf16")
+    U.compare("dV", dv, rv, "bf16")
+
+
 def _onehot(N, d, chunk):
     """[N, d]: row j is e_(j - chunk*d) for keys j of chunk `chunk`, 0 elsewhere."""
     m = np.zeros((N, d))

@@ -72,6 +72,25 @@ def test_sparse_small(dtype, d, N, causal, pad):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_sparse_wide_grid(d, causal):
+    """B*H*ceil(N/128) = 768 dK/dV workgroups (head_dim 64: the one-wave dK/dV kernel)."""
+    N = 300
+    w, inp = workloads.custom(8, 32, N, d, "bf16", causal, kv_range=(1, N), seed=550 + d)
+    m = _mask(N, 0.6, 551 + d, empty_row=1)
+    U.say(f"[sparse] wide grid N={N} d={d} causal={causal} mask={m.tolist()}")
+    o, lse, (dq, dk, dv) = _run(inp, m)
+    q, k, v, do = (U.f64(inp, n) for n in ("q", "k", "v", "dout"))
+    kvn = U.kv_np(inp)
+    ref_o, ref_l = oracle.attention_forward_sparse(q, k, v, inp["scale"], causal, kvn, m, BLK)
+    _check_fwd(o, lse, ref_o, ref_l, "bf16")
+    rq, rk, rv = oracle.attention_backward_sparse(q, k, v, do, inp["scale"], causal, kvn, m, BLK)
+    U.compare("dQ", dq, rq, "bf16")
+    U.compare("dK", dk, rk, "bf16")
+    U.compare("dV", dv, rv, "bf16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_all_ones_mask_matches_dense(d):
     w, inp = workloads.custom(2, 3, 300, d, "bf16", True, kv_range=(100, 300), seed=77)
     dev = U.to_dev(inp)
