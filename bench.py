@@ -401,9 +401,14 @@ def split_kv(fa, torch, workloads):
     """Supplementary lines: fa_fwd_partial + fa_merge against fa_fwd on shapes with few
     query blocks per CU (where splitting the key axis adds workgroups) and on the
     benchmarked shape. Outputs are preallocated; the merge's HBM rate is its
-    algorithmic bytes (n_splits*(d+1) floats read, d+1 written per row) over its time."""
-    shapes = [(1, 4, 8192, 128, False), (1, 8, 16384, 64, False), (2, 16, 4096, 128, True)]
+    algorithmic bytes (n_splits*(d+1) floats read, d+1 written per row) over its time.
+    After each shape's lines, one `split_hint` line compares the split fa_split_hint
+    recommends (0: unsplit) with the fastest of the options timed."""
+    shapes = [(1, 4, 8192, 128, False), (1, 4, 8192, 128, True), (1, 2, 16384, 128, True),
+              (1, 8, 4096, 128, True), (1, 8, 16384, 64, False), (1, 4, 16384, 64, True),
+              (1, 8, 8192, 128, False), (1, 16, 8192, 128, True), (2, 16, 4096, 128, True)]
     for B, H, N, d, causal in shapes:
+        times = {}
         w, inp = workloads.custom(B, H, N, d, "bf16", causal, seed=0, with_dout=False)
         dev = {n: inp[n].cuda() for n in ("q", "k", "v")}
         o = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
@@ -419,6 +424,7 @@ def split_kv(fa, torch, workloads):
             merge = lambda: fa.fa_merge(o_p, l_p, out=o, lse=lse)
             t_part = _time(torch, part)
             t_merge = _time(torch, merge)
+            times[split_len] = t_part + t_merge
             merge_bytes = 4.0 * B * H * N * (P * (d + 1) + (d + 1))
             print(json.dumps({
                 "split_kv": True, "B": B, "H": H, "N": N, "d": d, "causal": causal,
@@ -432,6 +438,16 @@ def split_kv(fa, torch, workloads):
                 "merge_hbm_frac": round(merge_bytes / t_merge / 1e6 / PEAK_HBM_GBS, 4)}),
                 flush=True)
             del o_p, l_p
+        hint = fa.fa_split_hint(B, H, N, d, causal=causal)
+        times[0] = t_full
+        best = min(times, key=times.get)
+        print(json.dumps({
+            "split_hint": True, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+            "hint_split_len": hint, "hint_ms": round(times.get(hint, float("nan")), 4),
+            "unsplit_ms": round(t_full, 4), "best_split_len": best,
+            "best_ms": round(times[best], 4),
+            "hint_over_best": round(times.get(hint, float("nan")) / times[best], 3)}),
+            flush=True)
 
 
 def sparse(fa, torch, workloads):

@@ -14,6 +14,7 @@ fa_bwd):
     fa_bwd_stage(stage, q, k, v, o, dout, lse, dq, dk, dv, workspace, *, ...) -> None
     fa_bwd_workspace_size(B, H, N, d) -> int
     fa_split_count(N, split_len) -> int
+    fa_split_hint(B, H, N, d, *, causal=False, dtype=torch.bfloat16) -> int (0: unsplit)
     fa_fwd_partial(q, k, v, *, split_len, causal=False, scale=None, kv_len=None)
         -> (o_part [P,B,H,N,d], lse_part [P,B,H,N])
     fa_merge(o_part, lse_part) -> (o, lse)
@@ -34,7 +35,7 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "fa_fwd", "fa_bwd", "fa_bwd_noalloc", "FA_NOALLOC_SCRATCH_BYTES", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_split_count", "fa_fwd_partial",
+__all__ = ["fwd", "bwd", "fa_fwd", "fa_bwd", "fa_bwd_noalloc", "FA_NOALLOC_SCRATCH_BYTES", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_split_count", "fa_split_hint", "fa_fwd_partial",
            "fa_merge", "fa_fwd_sparse", "fa_bwd_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
            "fa_fwd_deferred", "fa_dropout_threshold", "FA_DEFERRED_MAX_N", "FA_SPARSE_BLOCK", "fa_status_str", "fa_last_error", "fa_version", "FaError", "lib_path",
            "load_library",
@@ -85,6 +86,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_split_count.argtypes = [i32, i32]
     lib.fa_split_count.restype = i32
+    lib.fa_split_hint.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.fa_split_hint.restype = i32
     lib.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, i32, vp,
                                    i32, vp]
     lib.fa_fwd_partial.restype = i32
@@ -143,6 +146,16 @@ def fa_dropout_threshold(p: float) -> int:
 
 def fa_split_count(N: int, split_len: int) -> int:
     return int(load_library().fa_split_count(N, split_len))
+
+
+def fa_split_hint(B: int, H: int, N: int, d: int, *, causal: bool = False,
+                  dtype: torch.dtype = torch.bfloat16) -> int:
+    if dtype not in _DTYPE_CODE:
+        raise TypeError(f"dtype {dtype} is not float32, bfloat16 or float16")
+    r = int(load_library().fa_split_hint(B, H, N, d, int(bool(causal)), _DTYPE_CODE[dtype]))
+    if r < 0:
+        _check(-r)
+    return r
 
 
 def _check(status: int):

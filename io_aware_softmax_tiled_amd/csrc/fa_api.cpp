@@ -237,6 +237,13 @@ int fa_split_count(int N, int split_len) {
   return (int)(((long long)N + split_len - 1) / split_len);
 }
 
+int fa_split_hint(int B, int H, int N, int d, int causal, int dtype) {
+  clear_error();
+  const int st = check_common(B, H, N, d, 1.0f, dtype);
+  if (st != FA_OK) return -st;
+  return fa::fwd_split_hint(B, H, N, d, causal ? 1 : 0, dtype, fa::device_cu_count());
+}
+
 int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part,
                    float* lse_part, int B, int H, int N, int d, float scale, int causal,
                    int dtype, const int32_t* kv_len, int split_len, void* stream) {

@@ -51,6 +51,9 @@ FwdGrid fwd_grid(int B, int H, int N, int waves);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // compute units of the current device (read once per process; 256 if the query fails)
 int device_cu_count();
+// split_len recommended for the split-KV forward on a device with `cus` compute units
+// (0: run the unsplit forward)
+int fwd_split_hint(int B, int H, int N, int d, int causal, int dtype, int cus);
 // forward with the P V product deferred to the end of each query block's key row
 // (bf16/f16, d in {64, 128}, N <= kDeferredMaxN); split, block mask and dropout unused
 constexpr int kDeferredMaxN = 512;

@@ -25,6 +25,8 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t) { ++g_fwd_calls; g_last_fwd
 hipError_t launch_fwd_deferred(const FwdArgs& a, hipStream_t) { ++g_fwd_calls; g_last_fwd = a; return g_launch_result; }
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t, int stages) { ++g_bwd_calls; g_last_bwd = a; g_bwd_stages = stages; return g_launch_result; }
 hipError_t launch_merge(const MergeArgs&, hipStream_t) { ++g_merge_calls; return g_launch_result; }
+int device_cu_count() { return 256; }
+int fwd_split_hint(int, int, int, int, int, int, int) { return 0; }
 size_t bwd_delta_bytes(int B, int H, int N) {
   const size_t bytes = (size_t)B * H * N * sizeof(float);
   return (bytes + 255) / 256 * 256;

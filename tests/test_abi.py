@@ -35,7 +35,7 @@ def test_header_declares_the_api():
                                   "fa_bwd_workspace_size", "fa_dropout_threshold",
                                   "fa_fwd", "fa_fwd_deferred", "fa_fwd_dropout", "fa_fwd_partial",
                                   "fa_fwd_sparse",
-                                  "fa_last_error", "fa_merge", "fa_split_count",
+                                  "fa_last_error", "fa_merge", "fa_split_count", "fa_split_hint",
                                   "fa_status_str", "fa_version"]
 
 

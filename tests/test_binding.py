@@ -75,3 +75,38 @@ def test_cpu_inputs_are_refused_before_the_library(call):
             fa.fa_fwd_dropout(q, q, q, p=0.1, seed=1)
         else:
             fa.fa_fwd_deferred(q, q, q)
+
+
+# (B, H, N, d, causal) -> split_len on a 256-compute-unit device (the CPU run assumes
+# 256 when no device is visible; the MI355X has 256)
+SPLIT_HINTS = [
+    ((1, 4, 8192, 128, False), 4096),   # 128 query-block workgroups: two splits
+    ((1, 4, 8192, 128, True), 2048),    # causal, 128 workgroups: four splits
+    ((1, 8, 4096, 128, True), 1024),    # four splits of 1024 keys
+    ((1, 16, 2048, 128, False), 1024),  # two splits, the 1024-key floor
+    ((1, 2, 2048, 128, True), 1024),    # four would be 512 keys: two
+    ((1, 4, 16384, 64, True), 4096),    # 256 causal workgroups: four splits
+    ((1, 4, 16384, 64, False), 0),      # 256 workgroups without the mask: unsplit
+    ((1, 8, 8192, 128, False), 0),      # one workgroup per compute unit: unsplit
+    ((1, 16, 8192, 128, True), 0),      # 512 causal workgroups: unsplit
+    ((2, 16, 4096, 128, True), 0),      # the benchmarked shape: unsplit
+    ((4, 12, 1024, 64, True), 0),       # N < 2048: unsplit
+]
+
+
+@pytest.mark.parametrize("shape,expect", SPLIT_HINTS)
+def test_split_hint_rule(shape, expect):
+    B, H, N, d, causal = shape
+    h = fa.fa_split_hint(B, H, N, d, causal=causal)
+    assert h == expect
+    if h:
+        assert h % 64 == 0 and h >= 1024 and fa.fa_split_count(N, h) in (2, 4)
+
+
+def test_split_hint_f32_and_rejections():
+    assert fa.fa_split_hint(1, 4, 8192, 128, dtype=torch.float32) == 0
+    with pytest.raises(fa.FaError, match="head_dim 96"):
+        fa.fa_split_hint(1, 4, 8192, 96)
+    assert fa.fa_split_hint(0, 4, 8192, 128) == 0  # empty problem: nothing to split
+    with pytest.raises(fa.FaError):
+        fa.fa_split_hint(-1, 4, 8192, 128)

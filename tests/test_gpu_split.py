@@ -123,3 +123,21 @@ def test_split_full_size(split_len):
             rp_o, rp_l = oracle.head_forward_range(q[b, h], k[b, h], v[b, h], w.scale,
                                                    w.causal, None, kb, ke)
             _compare_partials(o_p[p, b, h], l_p[p, b, h], rp_o, rp_l, "bf16")
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 2, 2048, 128, True), (1, 2, 2048, 64, False)])
+def test_split_hint_path_matches_oracle(B, H, N, d, causal):
+    """The split fa_split_hint recommends, run as fa_fwd_partial + fa_merge, gives the
+    oracle's O and LSE (the hint is nonzero on both shapes: few query blocks)."""
+    h = fa.fa_split_hint(B, H, N, d, causal=causal)
+    assert h > 0
+    w, inp = workloads.custom(B, H, N, d, "bf16", causal, seed=900 + d, with_dout=False)
+    U.say(f"[split] hint B={B} H={H} N={N} d={d} causal={causal} split_len={h}")
+    o_p, l_p = _gpu_partial(inp, h)
+    o, lse = fa.fa_merge(o_p, l_p)
+    torch.cuda.synchronize()
+    ref = U.oracle_fwd(inp, workers=1)
+    ro = np.stack([[ref[(b, hh)][0] for hh in range(H)] for b in range(B)])
+    rl = np.stack([[ref[(b, hh)][1] for hh in range(H)] for b in range(B)])
+    U.compare("O", o, ro, "bf16")
+    U.compare("LSE", lse, rl, "bf16")
