@@ -794,42 +794,6 @@ __global__ __launch_bounds__(KS * 64, 1) void fwd_kernel_f32(
 
 }  // namespace
 
-// 8-wave workgroups when they still give at least one workgroup per CU
-static int fwd_waves(int B, int H, int N, int d, int dtype) {
-  if (dtype == kDtypeF32) return 4;
-  if (d == 128) return 8;
-  const long long blocks8 = (long long)B * H * ((N + 255) / 256);
-  return blocks8 >= 256 ? 8 : 4;
-}
-
-// Key length per split that fa_fwd_partial + fa_merge should use instead of the unsplit
-// forward, or 0 to run it unsplit. Splitting pays when the unsplit grid of query-block
-// workgroups leaves compute units idle: without a causal mask from half a workgroup per
-// compute unit down (two splits), under it from one per compute unit down (four
-// splits: the longest blocks of a causal grid are split too), keeping at least 1024
-// keys per split. Measured on the MI355X (unsplit against split totals, partials plus
-// merge): 1x4x8192 d=128 188 -> 143 us (2 splits), causal 184 -> 94 us (4); 1x2x16384
-// d=128 365 -> 264 us, causal 358 -> 154 us; 1x8x4096 d=128 100 -> 82 us, causal
-// 98 -> 64 us; 1x4x16384 d=64 causal 274 -> 215 us; at 256 non-causal workgroups
-// (1x8x8192 d=128: 249 against 275 us) or 384 and more causal ones the unsplit
-// kernel is as fast or faster.
-int fwd_split_hint(int B, int H, int N, int d, int causal, int dtype, int cus) {
-  if (dtype == kDtypeF32 || N < 2048 || B <= 0 || H <= 0 || cus <= 0) return 0;
-  const int waves = fwd_waves(B, H, N, d, dtype);
-  const long long rows = 32LL * waves;
-  const long long wgs = (long long)B * H * ((N + rows - 1) / rows);
-  int P = 1;
-  if (causal) {
-    if (wgs <= cus) P = 4;
-  } else if (2 * wgs <= cus) {
-    P = 2;
-  }
-  while (P > 1 && N / P < 1024) P /= 2;
-  if (P == 1) return 0;
-  const int per = (N + P - 1) / P;
-  return (per + 63) / 64 * 64;
-}
-
 FwdGrid fwd_grid(int B, int H, int N, int waves) {
   FwdGrid g;
   g.n_mblk = (N + 32 * waves - 1) / (32 * waves);

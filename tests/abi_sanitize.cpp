@@ -26,7 +26,6 @@ hipError_t launch_fwd_deferred(const FwdArgs& a, hipStream_t) { ++g_fwd_calls; g
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t, int stages) { ++g_bwd_calls; g_last_bwd = a; g_bwd_stages = stages; return g_launch_result; }
 hipError_t launch_merge(const MergeArgs&, hipStream_t) { ++g_merge_calls; return g_launch_result; }
 int device_cu_count() { return 256; }
-int fwd_split_hint(int, int, int, int, int, int, int) { return 0; }
 size_t bwd_delta_bytes(int B, int H, int N) {
   const size_t bytes = (size_t)B * H * N * sizeof(float);
   return (bytes + 255) / 256 * 256;
@@ -85,6 +84,15 @@ static void abi_forward() {
   CHECK(fa_fwd_partial(P(0), P(1), P(2), (float*)P(3), (float*)P(4), B, H, N, d, 0.1f, 0, FA_BF16, nullptr, 64, nullptr) == FA_OK);
   CHECK(g_last_fwd.split_len == 64);
   CHECK(fa_split_count(100, 64) == 2 && fa_split_count(INT_MAX, 64) == (int)((INT_MAX + 63LL) / 64) && fa_split_count(5, 0) == -1);
+  // the split rule (256 compute units): two splits without the mask at <= 128 query-block
+  // workgroups, four under it at <= 256, >= 1024 keys per split; extremes stay in range
+  CHECK(fa_split_hint(1, 4, 8192, 128, 0, FA_BF16) == 4096 && fa_split_hint(1, 4, 8192, 128, 1, FA_BF16) == 2048);
+  CHECK(fa_split_hint(1, 2, 2048, 128, 1, FA_BF16) == 1024 && fa_split_hint(2, 16, 4096, 128, 1, FA_BF16) == 0);
+  CHECK(fa_split_hint(1, 4, 8192, 128, 0, FA_F32) == 0 && fa_split_hint(0, 4, 8192, 128, 0, FA_BF16) == 0);
+  CHECK(fa_split_hint(1, 1, 65536, 128, 1, FA_F16) == 16384 && fa_split_hint(1, 1, 65536 + 256, 128, 1, FA_BF16) == 0);
+  CHECK(fa_split_hint(1, 1, (1 << 22) - 1, 128, 0, FA_BF16) == 0 && fa_split_hint(65535, 1, 4096, 64, 1, FA_BF16) == 0);
+  CHECK(fa_split_hint(-1, 4, 8192, 128, 0, FA_BF16) == -FA_EINVAL && fa_split_hint(1, 4, 8192, 96, 0, FA_BF16) == -FA_EUNSUPPORTED);
+  CHECK(fa_split_hint(1, 4, (1 << 22) + 1, 128, 0, FA_BF16) == -FA_EINVAL);
   CHECK(fa_fwd_sparse(P(0), P(1), P(2), (float*)P(3), (float*)P(4), B, H, N, d, 0.1f, 0, FA_BF16, nullptr, nullptr, nullptr) == FA_EINVAL);
   CHECK(fa_fwd_sparse(P(0), P(1), P(2), (float*)P(3), (float*)P(4), B, H, N, d, 0.1f, 0, FA_BF16, nullptr, (const uint8_t*)P(5), nullptr) == FA_OK);
   CHECK(fa_fwd_sparse(P(0), P(1), P(2), (float*)P(3), (float*)P(4), B, H, FA_SPARSE_MAX_N + 1, d, 0.1f, 0, FA_BF16, nullptr, (const uint8_t*)P(5), nullptr) == FA_EINVAL);
