@@ -59,6 +59,24 @@ def test_fwd_small(dtype, d, N, causal, pad):
     U.compare("LSE", lse, rl, dtype)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,pad", [(False, False), (True, False), (True, True)])
+def test_fwd_f32_many_subblocks_per_wave(d, causal, pad):
+    """fp32 at N = 1500 with Q x4: each wave of the key-split workgroup takes several
+    32-key sub-blocks (raising its reference maximum between them) and the waves' partial
+    states, with different maxima, are combined at the end."""
+    N = 1500
+    w, inp = workloads.custom(1, 2, N, d, "f32", causal, kv_range=(N // 2, N) if pad else None,
+                              q_mult=4.0, seed=60 + d, with_dout=False)
+    U.say(f"[fwd] f32 N={N} d={d} causal={causal} pad={pad}")
+    o, lse = U.gpu_fwd(inp)
+    ref = U.oracle_fwd(inp, workers=1)
+    ro = np.stack([ref[(0, h)][0] for h in range(2)])[None]
+    rl = np.stack([ref[(0, h)][1] for h in range(2)])[None]
+    U.compare("O", o, ro, "f32")
+    U.compare("LSE", lse, rl, "f32")
+
+
 def test_fwd_peaky_rows_and_many_tiles():
     """Q scaled x4 (peaky rows that exercise the rescale) over 1000 keys, bf16, d=128."""
     w, inp = workloads.custom(1, 4, 1000, 128, "bf16", True, q_mult=4.0, seed=7,
