@@ -403,7 +403,8 @@ def split_kv(fa, torch, workloads):
     benchmarked shape. Outputs are preallocated; the merge's HBM rate is its
     algorithmic bytes (n_splits*(d+1) floats read, d+1 written per row) over its time.
     After each shape's lines, one `split_hint` line compares the split fa_split_hint
-    recommends (0: unsplit) with the fastest of the options timed."""
+    recommends (0: unsplit) with the fastest of the options timed, and times fa_fwd_auto
+    (the same choice in one call, through a preallocated workspace)."""
     shapes = [(1, 4, 8192, 128, False), (1, 4, 8192, 128, True), (1, 2, 16384, 128, True),
               (1, 8, 4096, 128, True), (1, 8, 8192, 128, True), (1, 2, 8192, 64, False),
               (2, 2, 16384, 64, True), (1, 8, 16384, 64, False), (1, 4, 16384, 64, True),
@@ -442,13 +443,19 @@ def split_kv(fa, torch, workloads):
         hint = fa.fa_split_hint(B, H, N, d, causal=causal)
         times[0] = t_full
         best = min(times, key=times.get)
+        ws_bytes = fa.fa_fwd_workspace_size(B, H, N, d, causal=causal)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
+        t_auto = _time(torch, lambda: fa.fa_fwd_auto(dev["q"], dev["k"], dev["v"], causal=causal,
+                                                     scale=w.scale, out=o, lse=lse, workspace=ws))
         print(json.dumps({
             "split_hint": True, "B": B, "H": H, "N": N, "d": d, "causal": causal,
             "hint_split_len": hint, "hint_ms": round(times.get(hint, float("nan")), 4),
+            "auto_ms": round(t_auto, 4), "workspace_bytes": ws_bytes,
             "unsplit_ms": round(t_full, 4), "best_split_len": best,
             "best_ms": round(times[best], 4),
             "hint_over_best": round(times.get(hint, float("nan")) / times[best], 3)}),
             flush=True)
+        del ws
 
 
 def sparse(fa, torch, workloads):

@@ -148,6 +148,23 @@ FA_API int fa_split_count(int N, int split_len);
 FA_API int fa_split_hint(int B, int H, int N, int d, int causal, int dtype);
 
 /*
+ * The forward pass with the split chosen for it: fa_fwd when fa_split_hint gives 0 (or
+ * workspace is NULL), otherwise fa_fwd_partial with that split_len into the workspace
+ * followed by fa_merge into o and lse, which gives fa_fwd's O and LSE up to rounding (the
+ * combination rule above). fa_fwd_workspace_size: the bytes the split needs, the
+ * partials of n_splits = fa_split_count(N, split_len) ranges (0 when there is no split;
+ * also 0 for arguments fa_fwd would reject). The workspace is caller-owned device
+ * memory, 256-byte aligned, not overlapping any input or output; smaller than
+ * fa_fwd_workspace_size gives FA_EINVAL. Other arguments, limits and errors as fa_fwd,
+ * fa_fwd_partial and fa_merge; both kernels go to `stream` in that order.
+ */
+FA_API size_t fa_fwd_workspace_size(int B, int H, int N, int d, int causal, int dtype);
+FA_API int fa_fwd_auto(const void* q, const void* k, const void* v, float* o, float* lse,
+                int B, int H, int N, int d, float scale, int causal, int dtype,
+                const int32_t* kv_len, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/*
  * Partial forward pass over key ranges. Range p holds keys
  * [p*split_len, min(N, (p+1)*split_len)); visibility inside it is the usual one
  * (causal, kv_len). For each range p and query row, writes the normalised partial

@@ -15,6 +15,9 @@ fa_bwd):
     fa_bwd_workspace_size(B, H, N, d) -> int
     fa_split_count(N, split_len) -> int
     fa_split_hint(B, H, N, d, *, causal=False, dtype=torch.bfloat16) -> int (0: unsplit)
+    fa_fwd_workspace_size(B, H, N, d, *, causal=False, dtype=torch.bfloat16) -> int
+    fa_fwd_auto(q, k, v, *, causal=False, scale=None, kv_len=None, workspace=None)
+        -> (o, lse): fa_fwd, or the split fa_split_hint recommends, through a workspace
     fa_fwd_partial(q, k, v, *, split_len, causal=False, scale=None, kv_len=None)
         -> (o_part [P,B,H,N,d], lse_part [P,B,H,N])
     fa_merge(o_part, lse_part) -> (o, lse)
@@ -35,7 +38,7 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "fa_fwd", "fa_bwd", "fa_bwd_noalloc", "FA_NOALLOC_SCRATCH_BYTES", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_split_count", "fa_split_hint", "fa_fwd_partial",
+__all__ = ["fwd", "bwd", "fa_fwd", "fa_bwd", "fa_bwd_noalloc", "FA_NOALLOC_SCRATCH_BYTES", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_split_count", "fa_split_hint", "fa_fwd_workspace_size", "fa_fwd_auto", "fa_fwd_partial",
            "fa_merge", "fa_fwd_sparse", "fa_bwd_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
            "fa_fwd_deferred", "fa_dropout_threshold", "FA_DEFERRED_MAX_N", "FA_SPARSE_BLOCK", "fa_status_str", "fa_last_error", "fa_version", "FaError", "lib_path",
            "load_library",
@@ -88,6 +91,11 @@ def load_library() -> ctypes.CDLL:
     lib.fa_split_count.restype = i32
     lib.fa_split_hint.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.fa_split_hint.restype = i32
+    lib.fa_fwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.fa_fwd_workspace_size.restype = sz
+    lib.fa_fwd_auto.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, i32, vp, vp,
+                                sz, vp]
+    lib.fa_fwd_auto.restype = i32
     lib.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, i32, vp,
                                    i32, vp]
     lib.fa_fwd_partial.restype = i32
@@ -252,6 +260,40 @@ def fa_fwd(q, k, v, *, causal=False, scale=None, kv_len=None, out=None, lse=None
         st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d, scale,
                         int(bool(causal)), _DTYPE_CODE[q.dtype], _ptr(kv),
                         _stream(q.device, stream))
+    _check(st)
+    return o, lse_t
+
+
+def fa_fwd_workspace_size(B: int, H: int, N: int, d: int, *, causal: bool = False,
+                          dtype: torch.dtype = torch.bfloat16) -> int:
+    if dtype not in _DTYPE_CODE:
+        raise TypeError(f"dtype {dtype} is not float32, bfloat16 or float16")
+    return int(load_library().fa_fwd_workspace_size(B, H, N, d, int(bool(causal)),
+                                                    _DTYPE_CODE[dtype]))
+
+
+def fa_fwd_auto(q, k, v, *, causal=False, scale=None, kv_len=None, out=None, lse=None,
+                workspace=None, stream=None):
+    """Forward pass with the split fa_split_hint recommends (none: fa_fwd): returns
+    (o float32 [B,H,N,d], lse float32 [B,H,N]). The workspace (uint8, at least
+    fa_fwd_workspace_size bytes) is allocated when not given."""
+    B, H, N, d = _shape(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    kv = _kv(kv_len, B, q.device)
+    o = _out(out, "out", (B, H, N, d), q.device)
+    lse_t = _out(lse, "lse", (B, H, N), q.device)
+    need = fa_fwd_workspace_size(B, H, N, d, causal=causal, dtype=q.dtype)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    elif (not isinstance(workspace, torch.Tensor) or workspace.device != q.device
+          or not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous tensor on {q.device}")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_auto(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d, scale,
+                             int(bool(causal)), _DTYPE_CODE[q.dtype], _ptr(kv), _ptr(workspace),
+                             ws_bytes, _stream(q.device, stream))
     _check(st)
     return o, lse_t
 

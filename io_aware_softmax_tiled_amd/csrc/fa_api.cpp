@@ -319,6 +319,43 @@ int fa_merge(const float* o_part, const float* lse_part, float* o, float* lse, i
   return FA_OK;
 }
 
+size_t fa_fwd_workspace_size(int B, int H, int N, int d, int causal, int dtype) {
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  if (check_common(B, H, N, d, 1.0f, dtype) != FA_OK) return 0;
+  const int split_len = fa::fwd_split_hint(B, H, N, d, causal ? 1 : 0, dtype, fa::device_cu_count());
+  if (split_len <= 0) return 0;
+  const size_t P = (size_t)fa_split_count(N, split_len);
+  const size_t rows = (size_t)B * H * N;
+  return (P * rows * d * 4 + 255) / 256 * 256 + P * rows * 4;
+}
+
+int fa_fwd_auto(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                int H, int N, int d, float scale, int causal, int dtype, const int32_t* kv_len,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  int st = check_common(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  const size_t need = fa_fwd_workspace_size(B, H, N, d, causal, dtype);
+  if (need == 0 || workspace == nullptr)
+    return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, kv_len, nullptr, stream);
+  if (workspace_bytes < need)
+    return fail(FA_EINVAL, "workspace of %zu bytes is smaller than the %zu this shape needs",
+                workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(FA_EINVAL, "workspace is not 256-byte aligned");
+  const int split_len = fa::fwd_split_hint(B, H, N, d, causal ? 1 : 0, dtype, fa::device_cu_count());
+  const int P = fa_split_count(N, split_len);
+  const size_t rows = (size_t)B * H * N;
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             ((size_t)P * rows * d * 4 + 255) / 256 * 256);
+  // both calls check their own buffers: the partials (inside the workspace) against q, k,
+  // v and kv_len, and o and lse against the partials
+  st = fa_fwd_partial(q, k, v, o_part, lse_part, B, H, N, d, scale, causal, dtype, kv_len,
+                      split_len, stream);
+  if (st != FA_OK) return st;
+  return fa_merge(o_part, lse_part, o, lse, P, B, H, N, d, stream);
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
   return fa::bwd_workspace_bytes(B, H, N, d);

@@ -106,6 +106,26 @@ static void abi_forward() {
   CHECK(fa_merge((const float*)P(0), (const float*)P(1), (float*)P(2), (float*)P(3), 0, B, H, N, d, nullptr) == FA_EINVAL);
   CHECK(fa_merge((const float*)P(0), (const float*)P(1), (float*)P(2), (float*)P(3), 3, B, H, N, d, nullptr) == FA_OK);
   CHECK(g_merge_calls == 1);
+  // the forward with its split: unsplit without a workspace (or where no split pays),
+  // else partials into the workspace and the merge into o and lse
+  {
+    const int B2 = 1, H2 = 4, N2 = 8192, d2 = 128;
+    const size_t rows = (size_t)B2 * H2 * N2;
+    const size_t need = fa_fwd_workspace_size(B2, H2, N2, d2, 0, FA_BF16);
+    CHECK(need == (2 * rows * d2 * 4 + 255) / 256 * 256 + 2 * rows * 4);
+    CHECK(fa_fwd_workspace_size(2, 16, 4096, 128, 1, FA_BF16) == 0 && fa_fwd_workspace_size(1, 4, 8192, 96, 0, FA_BF16) == 0);
+    CHECK(fa_fwd_workspace_size(1, 4, 8192, 128, 0, FA_F32) == 0 && fa_fwd_workspace_size(0, 4, 8192, 128, 0, FA_BF16) == 0);
+    g_fwd_calls = 0;
+    g_merge_calls = 0;
+    CHECK(fa_fwd_auto(P(0), P(1), P(2), (float*)P(3), (float*)P(4), B2, H2, N2, d2, 0.1f, 0, FA_BF16, nullptr, nullptr, 0, nullptr) == FA_OK);
+    CHECK(g_fwd_calls == 1 && g_merge_calls == 0 && g_last_fwd.split_len == 0 && g_last_fwd.o == (float*)P(3));
+    CHECK(fa_fwd_auto(P(0), P(1), P(2), (float*)P(3), (float*)P(4), B2, H2, N2, d2, 0.1f, 0, FA_BF16, nullptr, P(5), need, nullptr) == FA_OK);
+    CHECK(g_fwd_calls == 2 && g_merge_calls == 1 && g_last_fwd.split_len == 4096 && g_last_fwd.o == (float*)P(5));
+    CHECK(fa_fwd_auto(P(0), P(1), P(2), (float*)P(3), (float*)P(4), B2, H2, N2, d2, 0.1f, 0, FA_BF16, nullptr, P(5), need - 1, nullptr) == FA_EINVAL);
+    CHECK(fa_fwd_auto(P(0), P(1), P(2), (float*)P(3), (float*)P(4), B2, H2, N2, d2, 0.1f, 0, FA_BF16, nullptr, P(5) + 16, need, nullptr) == FA_EINVAL);
+    CHECK(fa_fwd_auto(P(0), P(1), P(2), (float*)P(3), (float*)P(4), B2, H2, N2, d2, 0.1f, 0, FA_BF16, nullptr, P(0), need, nullptr) == FA_EINVAL);
+    CHECK(g_fwd_calls == 2 && g_merge_calls == 1);
+  }
 }
 
 static void abi_backward() {

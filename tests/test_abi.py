@@ -33,8 +33,8 @@ def test_header_declares_the_api():
     assert declared_symbols() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_noalloc", "fa_bwd_sparse",
                                   "fa_bwd_stage",
                                   "fa_bwd_workspace_size", "fa_dropout_threshold",
-                                  "fa_fwd", "fa_fwd_deferred", "fa_fwd_dropout", "fa_fwd_partial",
-                                  "fa_fwd_sparse",
+                                  "fa_fwd", "fa_fwd_auto", "fa_fwd_deferred", "fa_fwd_dropout", "fa_fwd_partial",
+                                  "fa_fwd_sparse", "fa_fwd_workspace_size",
                                   "fa_last_error", "fa_merge", "fa_split_count", "fa_split_hint",
                                   "fa_status_str", "fa_version"]
 

@@ -110,3 +110,16 @@ def test_split_hint_f32_and_rejections():
     assert fa.fa_split_hint(0, 4, 8192, 128) == 0  # empty problem: nothing to split
     with pytest.raises(fa.FaError):
         fa.fa_split_hint(-1, 4, 8192, 128)
+
+
+def test_fwd_workspace_size_follows_the_split():
+    """The split's partials: n_splits * B*H*N*d floats (256-byte aligned) + n_splits *
+    B*H*N floats; 0 where no split pays or the arguments are invalid."""
+    B, H, N, d = 1, 4, 8192, 128
+    for causal, P in ((False, 2), (True, 4)):
+        rows = B * H * N
+        assert fa.fa_fwd_workspace_size(B, H, N, d, causal=causal) == \
+            (P * rows * d * 4 + 255) // 256 * 256 + P * rows * 4
+    assert fa.fa_fwd_workspace_size(2, 16, 4096, 128, causal=True) == 0
+    assert fa.fa_fwd_workspace_size(1, 4, 8192, 128, dtype=torch.float32) == 0
+    assert fa.fa_fwd_workspace_size(1, 4, 8192, 96) == 0

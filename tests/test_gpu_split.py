@@ -141,3 +141,25 @@ def test_split_hint_path_matches_oracle(B, H, N, d, causal):
     rl = np.stack([[ref[(b, hh)][1] for hh in range(H)] for b in range(B)])
     U.compare("O", o, ro, "bf16")
     U.compare("LSE", lse, rl, "bf16")
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 2, 2048, 128, True), (1, 2, 2048, 64, False),
+                                            (1, 3, 300, 128, True)])
+def test_fwd_auto(B, H, N, d, causal):
+    """fa_fwd_auto: the hinted split through its workspace matches the oracle; where no split
+    pays (N = 300) it is fa_fwd, bit for bit."""
+    w, inp = workloads.custom(B, H, N, d, "bf16", causal, seed=950 + N + d, with_dout=False)
+    U.say(f"[split] auto B={B} H={H} N={N} d={d} causal={causal} "
+          f"workspace={fa.fa_fwd_workspace_size(B, H, N, d, causal=causal)}")
+    dev = U.to_dev(inp)
+    o, lse = fa.fa_fwd_auto(dev["q"], dev["k"], dev["v"], causal=causal, scale=inp["scale"])
+    torch.cuda.synchronize()
+    if fa.fa_split_hint(B, H, N, d, causal=causal) == 0:
+        o2, l2 = fa.fa_fwd(dev["q"], dev["k"], dev["v"], causal=causal, scale=inp["scale"])
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(lse, l2)
+    ref = U.oracle_fwd(inp, workers=1)
+    ro = np.stack([[ref[(b, hh)][0] for hh in range(H)] for b in range(B)])
+    rl = np.stack([[ref[(b, hh)][1] for hh in range(H)] for b in range(B)])
+    U.compare("O", o, ro, "bf16")
+    U.compare("LSE", lse, rl, "bf16")
