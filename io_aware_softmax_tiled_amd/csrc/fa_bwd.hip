@@ -399,20 +399,28 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages) {
   const bool dropout = a.drop_t >= 0;
   const float keep_scale = dropout ? 256.0f / (float)(256 - a.drop_t) : 1.0f;
   const uint32_t seed_lo = (uint32_t)a.seed, seed_hi = (uint32_t)(a.seed >> 32);
+  // head_dim 128 runs the dQ kernel with 8 waves (256 query rows per workgroup, each K/V
+  // tile serving twice the rows) unless that grid leaves compute units idle; head_dim 64
+  // and block-sparse patterns (one 128-row query block per workgroup) always run 4
+  const bool dq_narrow = (long long)BH * ((a.N + 255) / 256) < device_cu_count();
+#define FA_DQ_LAUNCH(TAG, DIM, WV, SP, DR)                                                    \
+  do {                                                                                       \
+    const int n_mblk = (a.N + 32 * WV - 1) / (32 * WV);                                      \
+    hipLaunchKernelGGL((bwd_dq_kernel<TAG, DIM, WV, SP, DR>), dim3(BH * n_mblk),              \
+                       dim3(64 * WV), 0, stream, q16, k16, v16, dO16, a.o, a.lse, a.delta,    \
+                       a.dmax, (stages & 8) ? 1 : 0, a.dq, BH, a.H, a.N, a.scale, sl2,        \
+                       a.causal, a.kv_len, n_mblk, hpx, a.block_mask, n_sb, seed_lo, seed_hi, \
+                       a.offset, a.drop_t, keep_scale);                                       \
+  } while (0)
 #define FA_BWD_LAUNCH2(TAG, DIM, SP, DR)                                                     \
   do {                                                                                       \
     if (stages & 1)                                                                          \
       hipLaunchKernelGGL((bwd_pre_kernel<TAG, DIM>), dim3(BH * n_groups), dim3(4 * DIM), 0,  \
                          stream, dO16, a.o, a.delta, a.dmax, a.N, n_groups);                  \
     if (stages & 4) {                                                                        \
-      constexpr int kW = (DIM == 128 && !SP) ? 8 : 4;                                        \
-      const int n_mblk = (a.N + 32 * kW - 1) / (32 * kW);                                    \
-      hipLaunchKernelGGL((bwd_dq_kernel<TAG, DIM, kW, SP, DR>), dim3(BH * n_mblk),            \
-                         dim3(64 * kW), 0, stream, q16, k16, v16, dO16, a.o, a.lse, a.delta,  \
-                         a.dmax, (stages & 8) ? 1 : 0, a.dq, BH, a.H, a.N, a.scale, sl2,      \
-                         a.causal,                                                            \
-                         a.kv_len, n_mblk, hpx, a.block_mask, n_sb, seed_lo, seed_hi,         \
-                         a.offset, a.drop_t, keep_scale);                                     \
+      constexpr int kWide = (DIM == 128 && !SP) ? 8 : 4;                                     \
+      if (dq_narrow) FA_DQ_LAUNCH(TAG, DIM, 4, SP, DR);                                      \
+      else FA_DQ_LAUNCH(TAG, DIM, kWide, SP, DR);                                            \
     }                                                                                        \
     if (stages & 2) {                                                                        \
       const hipError_t e = launch_bwd_dkdv(a, stream);                                       \
@@ -432,6 +440,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int stages) {
   }
 #undef FA_BWD_LAUNCH2
 #undef FA_BWD_LAUNCH
+#undef FA_DQ_LAUNCH
   return hipGetLastError();
 }
 
