@@ -823,7 +823,9 @@ static int persistent_grid(int items, int per_cu) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-  const int waves = fwd_waves(a.B, a.H, a.N, a.d, a.dtype);
+  const bool partial_or_sparse = a.split_len > 0 || a.block_mask != nullptr;
+  const int waves = (a.d == 128 && partial_or_sparse)
+                        ? 8 : fwd_waves(a.B, a.H, a.N, a.d, a.dtype, device_cu_count());
   const FwdGrid g = fwd_grid(a.B, a.H, a.N, waves);
   const auto* q16 = static_cast<const uint16_t*>(a.q);
   const auto* k16 = static_cast<const uint16_t*>(a.k);
@@ -846,11 +848,10 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
                      a.split_len, g.blocks, o_stride, lse_stride, a.block_mask, n_sb,      \
                      (uint32_t)a.seed, (uint32_t)(a.seed >> 32), a.offset, a.drop_t,       \
                      keep_scale, g.blocks * n_splits)
-  // head_dim 128 always runs 8 waves (its LDS use allows one workgroup per CU)
 #define FA_LAUNCH16(TAG, DIM, MODE)                                 \
   do {                                                              \
-    if (DIM == 128 || waves == 8) FA_LAUNCH16W(TAG, DIM, 8, MODE);  \
-    else FA_LAUNCH16W(TAG, 64, 4, MODE);                            \
+    if (waves == 8) FA_LAUNCH16W(TAG, DIM, 8, MODE);                \
+    else FA_LAUNCH16W(TAG, DIM, 4, MODE);                           \
   } while (0)
 #define FA_LAUNCH16P(TAG, DIM)                       \
   do {                                               \

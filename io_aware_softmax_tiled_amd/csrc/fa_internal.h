@@ -47,12 +47,17 @@ struct FwdGrid {
   int blocks;
 };
 
-// 8-wave workgroups when they still give at least one workgroup per CU
-inline int fwd_waves(int B, int H, int N, int d, int dtype) {
+// Waves per workgroup of the 16-bit forward (32 query rows each) on a device with `cus`
+// compute units: 8 when the 8-wave grid gives every compute unit a workgroup, else 4
+// (twice the workgroups). At head_dim 128 the LDS leaves room for one workgroup per
+// compute unit, so 4 waves pay only while all of them fit at once (8-wave grid at most
+// half the compute units: B=1 H=4 N=8192 187 -> 169 us, causal 183 -> 163 us, B=1 H=8
+// N=4096 causal 97 -> 86 us); the split-KV and block-sparse modes there keep 8.
+inline int fwd_waves(int B, int H, int N, int d, int dtype, int cus) {
   if (dtype == kDtypeF32) return 4;
-  if (d == 128) return 8;
   const long long blocks8 = (long long)B * H * ((N + 255) / 256);
-  return blocks8 >= 256 ? 8 : 4;
+  if (d == 128) return 2 * blocks8 <= cus ? 4 : 8;
+  return blocks8 >= cus ? 8 : 4;
 }
 
 // Key length per split that fa_fwd_partial + fa_merge should use instead of the unsplit
@@ -68,8 +73,8 @@ inline int fwd_waves(int B, int H, int N, int d, int dtype) {
 // kernel is as fast or faster.
 inline int fwd_split_hint(int B, int H, int N, int d, int causal, int dtype, int cus) {
   if (dtype == kDtypeF32 || N < 2048 || B <= 0 || H <= 0 || cus <= 0) return 0;
-  const int waves = fwd_waves(B, H, N, d, dtype);
-  const long long rows = 32LL * waves;
+  // (query-block workgroups counted as the split-KV kernel runs them: 8 waves at d = 128)
+  const long long rows = d == 128 ? 256 : 32LL * fwd_waves(B, H, N, d, dtype, cus);
   const long long wgs = (long long)B * H * ((N + rows - 1) / rows);
   int P = 1;
   if (causal) {
