@@ -408,7 +408,9 @@ def split_kv(fa, torch, workloads):
     shapes = [(1, 4, 8192, 128, False), (1, 4, 8192, 128, True), (1, 2, 16384, 128, True),
               (1, 8, 4096, 128, True), (1, 8, 8192, 128, True), (1, 2, 8192, 64, False),
               (2, 2, 16384, 64, True), (1, 8, 16384, 64, False), (1, 4, 16384, 64, True),
-              (1, 8, 8192, 128, False), (1, 16, 8192, 128, True), (2, 16, 4096, 128, True)]
+              (1, 16, 2048, 128, False), (1, 8, 4096, 128, False), (1, 8, 8192, 128, False),
+              (1, 16, 8192, 128, True),
+              (2, 16, 4096, 128, True)]
     for B, H, N, d, causal in shapes:
         times = {}
         w, inp = workloads.custom(B, H, N, d, "bf16", causal, seed=0, with_dout=False)

@@ -65,7 +65,9 @@ inline int fwd_waves(int B, int H, int N, int d, int dtype, int cus) {
 // workgroups leaves compute units idle: without a causal mask from half a workgroup per
 // compute unit down (two splits), under it from one per compute unit down (four
 // splits: the longest blocks of a causal grid are split too), keeping at least 1024
-// keys per split. Measured on the MI355X (unsplit against split totals, partials plus
+// keys per split under the mask and 2048 without it (where the unsplit forward of a
+// small grid runs 4-wave workgroups: 1x16x2048 d=128, two 1024-key splits 53 us against
+// 50 us unsplit). Measured on the MI355X (unsplit against split totals, partials plus
 // merge): 1x4x8192 d=128 188 -> 143 us (2 splits), causal 184 -> 94 us (4); 1x2x16384
 // d=128 365 -> 264 us, causal 358 -> 154 us; 1x8x4096 d=128 100 -> 82 us, causal
 // 98 -> 64 us; 1x4x16384 d=64 causal 274 -> 215 us; at 256 non-causal workgroups
@@ -82,7 +84,8 @@ inline int fwd_split_hint(int B, int H, int N, int d, int causal, int dtype, int
   } else if (2 * wgs <= cus) {
     P = 2;
   }
-  while (P > 1 && N / P < 1024) P /= 2;
+  const int min_keys = causal ? 1024 : 2048;
+  while (P > 1 && N / P < min_keys) P /= 2;
   if (P == 1) return 0;
   const int per = (N + P - 1) / P;
   return (per + 63) / 64 * 64;

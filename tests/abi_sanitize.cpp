@@ -85,9 +85,11 @@ static void abi_forward() {
   CHECK(g_last_fwd.split_len == 64);
   CHECK(fa_split_count(100, 64) == 2 && fa_split_count(INT_MAX, 64) == (int)((INT_MAX + 63LL) / 64) && fa_split_count(5, 0) == -1);
   // the split rule (256 compute units): two splits without the mask at <= 128 query-block
-  // workgroups, four under it at <= 256, >= 1024 keys per split; extremes stay in range
+  // workgroups, four under it at <= 256, >= 2048 keys per split (1024 under the mask);
+  // extremes stay in range
   CHECK(fa_split_hint(1, 4, 8192, 128, 0, FA_BF16) == 4096 && fa_split_hint(1, 4, 8192, 128, 1, FA_BF16) == 2048);
   CHECK(fa_split_hint(1, 2, 2048, 128, 1, FA_BF16) == 1024 && fa_split_hint(2, 16, 4096, 128, 1, FA_BF16) == 0);
+  CHECK(fa_split_hint(1, 16, 2048, 128, 0, FA_BF16) == 0 && fa_split_hint(1, 8, 4096, 128, 0, FA_BF16) == 2048);
   CHECK(fa_split_hint(1, 4, 8192, 128, 0, FA_F32) == 0 && fa_split_hint(0, 4, 8192, 128, 0, FA_BF16) == 0);
   CHECK(fa_split_hint(1, 1, 65536, 128, 1, FA_F16) == 16384 && fa_split_hint(1, 1, 65536 + 256, 128, 1, FA_BF16) == 0);
   CHECK(fa_split_hint(1, 1, (1 << 22) - 1, 128, 0, FA_BF16) == 0 && fa_split_hint(65535, 1, 4096, 64, 1, FA_BF16) == 0);

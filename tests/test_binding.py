@@ -83,8 +83,9 @@ SPLIT_HINTS = [
     ((1, 4, 8192, 128, False), 4096),   # 128 query-block workgroups: two splits
     ((1, 4, 8192, 128, True), 2048),    # causal, 128 workgroups: four splits
     ((1, 8, 4096, 128, True), 1024),    # four splits of 1024 keys
-    ((1, 16, 2048, 128, False), 1024),  # two splits, the 1024-key floor
-    ((1, 2, 2048, 128, True), 1024),    # four would be 512 keys: two
+    ((1, 16, 2048, 128, False), 0),     # two splits would hold 1024 keys: below 2048
+    ((1, 8, 4096, 128, False), 2048),   # two splits of 2048 keys
+    ((1, 2, 2048, 128, True), 1024),    # causal: four would be 512 keys, two hold 1024
     ((1, 4, 16384, 64, True), 4096),    # 256 causal workgroups: four splits
     ((1, 4, 16384, 64, False), 0),      # 256 workgroups without the mask: unsplit
     ((1, 8, 8192, 128, False), 0),      # one workgroup per compute unit: unsplit
@@ -100,7 +101,8 @@ def test_split_hint_rule(shape, expect):
     h = fa.fa_split_hint(B, H, N, d, causal=causal)
     assert h == expect
     if h:
-        assert h % 64 == 0 and h >= 1024 and fa.fa_split_count(N, h) in (2, 4)
+        assert h % 64 == 0 and h >= (1024 if causal else 2048)
+        assert fa.fa_split_count(N, h) in (2, 4)
 
 
 def test_split_hint_f32_and_rejections():
