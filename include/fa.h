@@ -140,8 +140,8 @@ FA_API int fa_split_count(int N, int split_len);
  * the unsplit forward's grid of query-block workgroups is at most half the compute
  * units (two splits), or, under the causal mask, at most one per compute unit (four
  * splits), with at least 2048 keys per split (1024 under the causal mask); f32 and N < 2048 always give 0. Host
- * only: reads the current device's compute-unit count (256 assumed if none is
- * visible) and launches nothing. Arguments as fa_fwd (scale not taken); B, H, N, d or
+ * only: reads the current device's compute-unit count (read once per process;
+ * 256 assumed if none is visible) and launches nothing. Arguments as fa_fwd (scale not taken); B, H, N, d or
  * dtype that fa_fwd would reject give the negated status (-FA_EINVAL or
  * -FA_EUNSUPPORTED; fa_last_error says which).
  */
