@@ -136,14 +136,15 @@ FA_API int fa_split_count(int N, int split_len);
  * fa_split_hint: the split_len for which fa_fwd_partial + fa_merge is expected to beat
  * fa_fwd on this device for a problem of this shape, or 0 when fa_fwd should run
  * unsplit (the split itself is the combination rule above; when to split is not on
- * the pages: the rule below is measured on the MI355X). A split is recommended when
- * the unsplit forward's grid of query-block workgroups is at most half the compute
- * units (two splits), or, under the causal mask, at most one per compute unit (four
- * splits), with at least 2048 keys per split (1024 under the causal mask); f32 and N < 2048 always give 0. Host
- * only: reads the current device's compute-unit count (read once per process;
- * 256 assumed if none is visible) and launches nothing. Arguments as fa_fwd (scale not taken); B, H, N, d or
- * dtype that fa_fwd would reject give the negated status (-FA_EINVAL or
- * -FA_EUNSUPPORTED; fa_last_error says which).
+ * the pages: the rule below is measured on the MI355X). Counting query-block
+ * workgroups of 256 rows at head_dim 128 and of the forward's own size at 64, a split
+ * is recommended when they are at most half the compute units (two splits) or, under
+ * the causal mask, at most one per compute unit (four splits), halving the count until
+ * every split holds at least 2048 keys (1024 under the causal mask); f32 and N < 2048
+ * always give 0. Host only: reads the current device's compute-unit count once per
+ * process (256 if none is visible) and launches nothing. Arguments as fa_fwd (scale not
+ * taken); B, H, N, d or dtype that fa_fwd would reject give the negated status
+ * (-FA_EINVAL or -FA_EUNSUPPORTED; fa_last_error says which).
  */
 FA_API int fa_split_hint(int B, int H, int N, int d, int causal, int dtype);
 
